@@ -1,0 +1,174 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+A step is one kda_prefill of the single-sequence workload (B=1, H=32,
+T=8192, D=128, C=64, bf16 q/k/v/o and beta, fp32 g and state), inputs
+already resident in HBM. The JSON line also carries the decode workload
+(512 sequences x 32 heads, D=128, 64 in-place steps) measured the same way,
+the roofline of the dominant kernel, and the fp64 CPU oracle timed on the
+host cores as a reference baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_delta_rule_103_amd import costs, inputs, kda_decode, kda_prefill  # noqa: E402
+from gated_delta_rule_103_amd.kda import kda_prefill_workspace_size  # noqa: E402
+
+PREFILL_WORKLOAD = "single_seq_8k"
+DECODE_WORKLOAD = "decode_512x32"
+# arithmetic type of the timed prefill path (bf16 MFMA contractions, fp32 accumulate/state)
+PREFILL_DTYPE = os.environ.get("KDA_BENCH_DTYPE_LABEL", "f32")
+
+
+def _time_region(fn, steps, warmup):
+    """Run warmup untimed, then time exactly `steps` calls with events on the
+    current stream (the one the library launches on), synchronised on both sides."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]          # ms per launch
+    return wall, per
+
+
+def bench_prefill(steps, warmup):
+    w = inputs.WORKLOADS[PREFILL_WORKLOAD]
+    p = inputs.workload_prefill(PREFILL_WORKLOAD, device="cuda")
+    B, T, H, D, C = w["B"], w["T"], w["H"], w["D"], w["C"]
+    out = torch.empty(B, T, H, D, dtype=torch.bfloat16, device="cuda")
+    S_out = torch.empty(B, H, D, D, dtype=torch.float32, device="cuda")
+    ws_n = kda_prefill_workspace_size(B, B * T, H, D, D, C, torch.bfloat16)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        kda_prefill(p.q, p.k, p.v, p.g, p.beta, None, out=out, S_out=S_out, C=C, workspace=ws)
+
+    wall, per = _time_region(step, steps, warmup)
+    tokens = B * T
+    ms = sum(per) / len(per)
+    flops = costs.prefill_flops(tokens, H, C, D)
+    min_bytes = costs.prefill_min_bytes(tokens, H, D, D, B, io_bytes=2, beta_bytes=2)
+    return dict(tokens=tokens, wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=ms,
+                per_launch_ms=per, flops=flops, min_bytes=min_bytes, inputs=p)
+
+
+def bench_decode(steps, warmup):
+    w = inputs.WORKLOADS[DECODE_WORKLOAD]
+    x = inputs.workload_decode(DECODE_WORKLOAD, device="cuda")
+    S = x.state.clone()
+    out = torch.empty(w["N"], w["H"], w["D"], dtype=torch.bfloat16, device="cuda")
+    nsteps = w["steps"]
+
+    def one_pass():
+        for s in range(nsteps):
+            kda_decode(x.q[s], x.k[s], x.v[s], x.g[s], x.beta[s], S, out=out)
+
+    wall, per = _time_region(one_pass, steps, warmup)
+    ms_step = (sum(per) / len(per)) / nsteps
+    N, H, D = w["N"], w["H"], w["D"]
+    state_bytes = costs.decode_bytes_per_head(D) * N * H
+    vec_bytes = costs.decode_vector_bytes(N, H, D, D)
+    return dict(ms_per_token_step=ms_step, state_bytes=state_bytes, vec_bytes=vec_bytes,
+                gbps_state=state_bytes / (ms_step * 1e-3) / 1e9,
+                gbps_total=(state_bytes + vec_bytes) / (ms_step * 1e-3) / 1e9,
+                frac_hbm=state_bytes / (ms_step * 1e-3) / 1e9 / costs.MI355X_PEAK["hbm_GBps"])
+
+
+def cpu_baseline(p):
+    """The fp64 oracle on the whole single-sequence workload (32 heads x 8192 tokens)."""
+    import oracle
+    H = p.q.shape[2]
+    f64 = lambda t: t.detach().cpu().double().numpy().reshape(-1, H, t.shape[-1])
+    q, k, v, g = (f64(t) for t in (p.q, p.k, p.v, p.g))
+    beta = p.beta.detach().cpu().double().numpy().reshape(-1, H)
+    threads = oracle.default_threads(H)
+    t0 = time.perf_counter()
+    oracle.recurrent(q, k, v, g, beta, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=q.shape[0] / dt / 1e6, unit="Mtok/s", cores=threads, kind="oracle",
+                sample=f"whole {PREFILL_WORKLOAD} workload: {H} heads x {q.shape[0]} tokens, fp64, "
+                       f"{dt:.2f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the KDA hot path runs on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    pf = bench_prefill(args.steps, args.warmup)
+    peak_tf = costs.MI355X_PEAK["bf16_TFLOPs"]
+    peak_bw = costs.MI355X_PEAK["hbm_GBps"]
+    k_s = pf["kernel_ms"] * 1e-3
+    tflops = pf["flops"] / k_s / 1e12
+    gbps = pf["min_bytes"] / k_s / 1e9
+    value = pf["tokens"] * args.steps / pf["wall_s"] / 1e6
+    dec = None if args.no_decode else bench_decode(max(1, args.steps // 4), 1)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(pf["inputs"])
+
+    w = inputs.WORKLOADS[PREFILL_WORKLOAD]
+    line = {
+        "metric": "KDA prefill Mtokens/s (H=32,D=128,C=64) + decode achieved HBM GB/s vs peak",
+        "value": round(value, 3),
+        "unit": "Mtok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": PREFILL_DTYPE,
+        "data": "synthetic",
+        "config": {"workload": PREFILL_WORKLOAD, "B": w["B"], "T": w["T"], "H": w["H"],
+                   "Dk": w["D"], "Dv": w["D"], "C": w["C"], "io": "bf16 q/k/v/o/beta, fp32 g/state",
+                   "gate": "-softplus(N(0,1)+2)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak_tf, 4), "traffic": None,
+                     "kernel": "kda_prefill (whole call)", "model": "12C^3+8C^2D+6CD^2 per chunk-head",
+                     "kernel_ms": round(pf["kernel_ms"], 4)},
+        "roofline_hbm": {"bound": "hbm", "achieved": round(gbps, 1), "peak": peak_bw, "unit": "GB/s",
+                         "frac": round(gbps / peak_bw, 4),
+                         "bytes": pf["min_bytes"], "model": "algorithmic minimum bytes per launch"},
+    }
+    if dec is not None:
+        line["decode"] = {"workload": DECODE_WORKLOAD, "ms_per_token_step": round(dec["ms_per_token_step"], 4),
+                          "roofline": {"bound": "hbm", "achieved": round(dec["gbps_state"], 1),
+                                       "peak": peak_bw, "unit": "GB/s",
+                                       "frac": round(dec["frac_hbm"], 4), "traffic": None,
+                                       "model": "8*D^2 bytes per head-step"},
+                          "gbps_incl_vectors": round(dec["gbps_total"], 1)}
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,9 @@
+"""MI355X-native Kimi Delta Attention (KDA): chunked/varlen prefill and decode.
+
+The compute lives in libkda.so (hand-written HIP kernels for gfx950 behind the
+C ABI of include/kda.h); ``kda`` is its ctypes binding.
+"""
+from .kda import (KDAError, kda_decode, kda_prefill, kda_prefill_workspace_size,  # noqa: F401
+                  load_library)
+
+__all__ = ["kda_prefill", "kda_decode", "kda_prefill_workspace_size", "load_library", "KDAError"]

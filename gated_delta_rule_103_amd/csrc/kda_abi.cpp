@@ -1,0 +1,95 @@
+// kda_abi.cpp -- the extern "C" boundary of libkda: argument checks,
+// workspace sizing and kernel selection. Declarations and the contract of
+// every entry point are in include/kda.h.
+#include "../../include/kda.h"
+
+#include <climits>
+
+#include "kda_launch.h"
+
+using kda::Dt;
+
+namespace {
+
+bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
+
+bool head_dims_supported(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk == 128); }
+
+bool chunk_supported(int C) { return C == 16 || C == 32 || C == 64; }
+
+// Which prefill kernels serve this dtype combination.
+bool use_mfma(kda_dtype io) { (void)io; return false; }
+
+size_t workspace_for(int N, long long T_total, int H, int Dk, int Dv, int C, kda_dtype io) {
+    return use_mfma(io) ? kda::prefill_mfma_workspace(N, T_total, H, Dk, Dv, C)
+                        : kda::prefill_f32_workspace(N, T_total, H, Dk, Dv, C);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char *kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        default: return "KDA_UNKNOWN_STATUS";
+    }
+}
+
+size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int C, kda_dtype io_dtype) {
+    if (N < 1 || T_total < 0 || H < 1 || !dtype_ok(io_dtype)) return 0;
+    if (!head_dims_supported(Dk, Dv) || !chunk_supported(C)) return 0;
+    return workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);
+}
+
+int kda_prefill(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B,
+                int T, int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
+                kda_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+    if (N < 1 || B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || C < 1) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(io_dtype) || !dtype_ok(beta_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
+    const long long T_total = (long long)B * T;
+    if (T_total > INT_MAX / 2 || (long long)N * H > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
+    if (!head_dims_supported(Dk, Dv) || !chunk_supported(C)) return KDA_ERR_UNSUPPORTED;
+    if (io_dtype == KDA_F32 && (beta_dtype != KDA_F32 || out_dtype != KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    const size_t need = workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KDA_ERR_WORKSPACE;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.out = out; a.S_out = S_out;
+    a.cu_seqlens = cu_seqlens; a.N = N; a.B = B; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv; a.C = C;
+    a.io = static_cast<Dt>(io_dtype); a.beta_dt = static_cast<Dt>(beta_dtype);
+    a.out_dt = static_cast<Dt>(out_dtype);
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = use_mfma(io_dtype) ? kda::launch_prefill_mfma(a) : kda::launch_prefill_f32(a);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
+               void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
+               kda_dtype out_dtype, void *stream) {
+    if (!q || !k || !v || !g || !beta || !S || !out) return KDA_ERR_INVALID_ARG;
+    if (N < 1 || H < 1 || Dk < 1 || Dv < 1) return KDA_ERR_INVALID_ARG;
+    if (!dtype_ok(io_dtype) || !dtype_ok(beta_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H > INT_MAX) return KDA_ERR_INVALID_ARG;
+    if (!head_dims_supported(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.out = out;
+    a.N = N; a.H = H; a.Dk = Dk; a.Dv = Dv;
+    a.io = static_cast<Dt>(io_dtype); a.beta_dt = static_cast<Dt>(beta_dtype);
+    a.out_dt = static_cast<Dt>(out_dtype);
+    a.stream = static_cast<hipStream_t>(stream);
+    return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

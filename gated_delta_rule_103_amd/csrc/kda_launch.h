@@ -1,0 +1,56 @@
+// kda_launch.h -- host-side launchers implemented in the .hip files and
+// called by the argument-checking layer in kda_abi.cpp. Every launcher
+// assumes its arguments were already validated and returns a hipError_t.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g;
+    const void *beta;
+    const float *S0;
+    void *out;
+    float *S_out;
+    const int32_t *cu_seqlens;  // device, or nullptr (dense)
+    int N, B, T, H, Dk, Dv, C;
+    Dt io, beta_dt, out_dt;
+    void *ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g;
+    const void *beta;
+    float *S;
+    void *out;
+    int N, H, Dk, Dv;
+    Dt io, beta_dt, out_dt;
+    hipStream_t stream;
+};
+
+// Upper bound on the number of chunks of all sequences (each sequence adds at
+// most one partial chunk).
+inline long long max_chunks(int N, long long T_total, int C) {
+    return (T_total + C - 1) / C + N;
+}
+
+// fp32-arithmetic chunked prefill (plan + prep + scan kernels).
+size_t prefill_f32_workspace(int N, long long T_total, int H, int Dk, int Dv, int C);
+hipError_t launch_prefill_f32(const PrefillArgs &a);
+
+// bf16 MFMA chunked prefill.
+size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C);
+hipError_t launch_prefill_mfma(const PrefillArgs &a);
+
+// single-token decode.
+hipError_t launch_decode(const DecodeArgs &a);
+
+}  // namespace kda

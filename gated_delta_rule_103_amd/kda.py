@@ -1,0 +1,125 @@
+"""Thin Python binding of libkda (ctypes): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+declared in ``include/kda.h``; this module turns torch tensors into device
+pointers, sizes and dtype codes, and raises on a non-zero status. PyTorch is
+used for device memory and streams only. There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+_STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
+           -3: "KDA_ERR_WORKSPACE", -4: "KDA_ERR_HIP"}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {_STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkda.so from the package directory (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(hipcc, gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_version.restype = i
+    lib.kda_version.argtypes = []
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_prefill.restype = i
+    lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                i, i, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.kda_decode.restype = i
+    lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libkda must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def kda_prefill_workspace_size(N: int, T_total: int, H: int, Dk: int, Dv: int, C: int,
+                               io_dtype: torch.dtype) -> int:
+    return int(load_library().kda_prefill_workspace_size(N, T_total, H, Dk, Dv, C, _DT[io_dtype]))
+
+
+def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
+                out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
+                return_state: bool = True):
+    """Chunked KDA prefill. q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
+    S0: [N, H, Dk, Dv] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B == 1) or None.
+    Returns (out [B, T, H, Dv], S_out [N, H, Dk, Dv] or None)."""
+    lib = load_library()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    od = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty(B, T, H, Dv, dtype=od, device=q.device)
+    if S_out is None and return_state:
+        S_out = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
+    need = int(lib.kda_prefill_workspace_size(N, B * T, H, Dk, Dv, C, _dt(q)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
+                         _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
+                         _dt(out), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_prefill")
+    return out, S_out
+
+
+def kda_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
+               stream=None):
+    """One decode step, state S [N, H, Dk, Dv] fp32 updated in place.
+    q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H]. Returns out [N, H, Dv]."""
+    lib = load_library()
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty(N, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
+    st = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
+                        N, H, Dk, Dv, _dt(q), _dt(beta), _dt(out), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_decode")
+    return out

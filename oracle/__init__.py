@@ -36,7 +36,7 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile ``kda_oracle.c`` into ``libkda_oracle.so`` with the host C compiler."""
     if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-std=c99",
+        cmd = ["gcc", "-O3", "-fPIC", "-shared", "-pthread", "-std=c99",
                "-o", _LIB + ".tmp", _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_LIB + ".tmp", _LIB)

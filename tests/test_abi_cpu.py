@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol declared in include/kda.h, and rejects bad arguments with the
+documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_103_amd import load_library
+    return load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for required in ("kda_prefill", "kda_decode", "kda_prefill_workspace_size",
+                     "kda_status_string", "kda_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(-3) == b"KDA_ERR_WORKSPACE"
+    assert lib.kda_status_string(99) == b"KDA_UNKNOWN_STATUS"
+
+
+def _prefill(lib, **kw):
+    fake = ctypes.c_void_p(256)          # never dereferenced: checks return first
+    a = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, S0=None, out=fake, S_out=None,
+             cu=None, N=1, B=1, T=64, H=2, Dk=64, Dv=64, C=16, io=1, bd=1, od=1,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.kda_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["out"], a["S_out"],
+                           a["cu"], a["N"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["C"],
+                           a["io"], a["bd"], a["od"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(beta=None), -1),
+    (dict(N=0), -1), (dict(H=0), -1), (dict(T=-1), -1), (dict(N=2), -1),
+    (dict(io=7), -1), (dict(od=3), -1),
+    (dict(cu=ctypes.c_void_p(512), B=2, N=2), -1),
+    (dict(Dk=96, Dv=96), -2), (dict(Dk=64, Dv=128), -2), (dict(C=8), -2), (dict(C=128), -2),
+    (dict(io=0, bd=1, od=0), -2), (dict(io=0, bd=0, od=1), -2),
+    (dict(ws=None, wsb=0), -3),
+    (dict(ws=ctypes.c_void_p(256), wsb=16), -3),
+])
+def test_prefill_argument_errors(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+
+
+def test_prefill_workspace_misaligned(lib):
+    need = lib.kda_prefill_workspace_size(1, 64, 2, 64, 64, 16, 1)
+    assert need > 0
+    assert _prefill(lib, ws=ctypes.c_void_p(4096 + 64), wsb=need) == -3
+
+
+def test_workspace_size_is_pure_and_rejects_bad_sizes(lib):
+    a = lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 1)
+    assert a == lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 1)
+    assert lib.kda_prefill_workspace_size(0, 100, 2, 64, 64, 16, 1) == 0
+    assert lib.kda_prefill_workspace_size(1, 100, 2, 96, 96, 16, 1) == 0
+    assert lib.kda_prefill_workspace_size(1, 100, 2, 64, 64, 12, 1) == 0
+
+
+def _decode(lib, **kw):
+    fake = ctypes.c_void_p(256)
+    a = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, S=fake, out=fake, N=4, H=2, Dk=128,
+             Dv=128, io=1, bd=1, od=1, stream=None)
+    a.update(kw)
+    return lib.kda_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["out"], a["N"],
+                          a["H"], a["Dk"], a["Dv"], a["io"], a["bd"], a["od"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=None), -1), (dict(out=None), -1), (dict(g=None), -1), (dict(N=0), -1),
+    (dict(H=-1), -1), (dict(io=5), -1), (dict(Dk=32, Dv=32), -2), (dict(Dk=128, Dv=64), -2),
+])
+def test_decode_argument_errors(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def test_cost_models_match_the_pages():
+    """The explainer's closed forms at (C, D) = (64, 128): 12C^3 + 8C^2 D + 6CD^2
+    FLOPs and 8C^2 + 22CD bytes per chunk per head; decode 7D^2 FLOPs, 8D^2 bytes."""
+    from gated_delta_rule_103_amd import costs
+    assert costs.prefill_flops_per_chunk(64, 128) == 13_631_488
+    assert costs.pages_prefill_bytes_per_chunk(64, 128) == 212_992
+    assert costs.prefill_flops(8192, 32, 64, 128) == 128 * 32 * 13_631_488
+    assert costs.decode_flops_per_head(128) == 114_688
+    assert costs.decode_bytes_per_head(128) == 131_072
+    assert costs.prefill_flops_per_chunk(16, 64) == 573_440
+    # minimum traffic per token-head at the bf16 workloads: 1538 bytes
+    assert costs.prefill_min_bytes(1, 1, 128, 128, 0, writes_state=False) == 1538
+
+
+def test_input_generators_are_deterministic():
+    from gated_delta_rule_103_amd import inputs
+    a = inputs.prefill(2, 64, B=1, T=40, io="bf16", seed=5, s0_std=0.02)
+    b = inputs.prefill(2, 64, B=1, T=40, io="bf16", seed=5, s0_std=0.02)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v), (a.g, b.g), (a.beta, b.beta), (a.S0, b.S0)):
+        assert x.dtype == y.dtype and bool((x == y).all())
+    import torch
+    n = a.q.float().norm(dim=-1)
+    assert float((n - 1).abs().max()) < 1e-2
+    assert float(a.g.max()) < 0
+    lens = inputs.varlen_lengths(16, 512, 16384, 1002)
+    assert len(lens) == 16 and min(lens) >= 512 and max(lens) <= 16384
+    assert lens == inputs.varlen_lengths(16, 512, 16384, 1002)
