@@ -27,8 +27,8 @@ from gated_delta_rule_103_amd.kda import kda_prefill_workspace_size  # noqa: E40
 
 PREFILL_WORKLOAD = "single_seq_8k"
 DECODE_WORKLOAD = "decode_512x32"
-# arithmetic type of the timed prefill path (bf16 MFMA contractions, fp32 accumulate/state)
-PREFILL_DTYPE = os.environ.get("KDA_BENCH_DTYPE_LABEL", "f32")
+# arithmetic type of the timed prefill path: bf16 MFMA contractions, fp32 accumulation and state
+PREFILL_DTYPE = "bf16"
 
 
 def _time_region(fn, steps, warmup):

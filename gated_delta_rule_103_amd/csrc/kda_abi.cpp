@@ -18,7 +18,7 @@ bool head_dims_supported(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk ==
 bool chunk_supported(int C) { return C == 16 || C == 32 || C == 64; }
 
 // Which prefill kernels serve this dtype combination.
-bool use_mfma(kda_dtype io) { (void)io; return false; }
+bool use_mfma(kda_dtype io) { return io == KDA_BF16; }
 
 size_t workspace_for(int N, long long T_total, int H, int Dk, int Dv, int C, kda_dtype io) {
     return use_mfma(io) ? kda::prefill_mfma_workspace(N, T_total, H, Dk, Dv, C)
@@ -58,6 +58,9 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g, con
     if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
     const long long T_total = (long long)B * T;
     if (T_total > INT_MAX / 2 || (long long)N * H > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
+    // q, k and g are read with 16-byte vector loads
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(g)) & 15u)
+        return KDA_ERR_INVALID_ARG;
     if (!head_dims_supported(Dk, Dv) || !chunk_supported(C)) return KDA_ERR_UNSUPPORTED;
     if (io_dtype == KDA_F32 && (beta_dtype != KDA_F32 || out_dtype != KDA_F32)) return KDA_ERR_UNSUPPORTED;
     const size_t need = workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);

@@ -42,6 +42,9 @@ inline long long max_chunks(int N, long long T_total, int C) {
     return (T_total + C - 1) / C + N;
 }
 
+// Device-side chunk table of packed sequences: chunk_off[n] for n <= N.
+hipError_t launch_chunk_plan(const int32_t *cu, int N, int C, int32_t *chunk_off, hipStream_t stream);
+
 // fp32-arithmetic chunked prefill (plan + prep + scan kernels).
 size_t prefill_f32_workspace(int N, long long T_total, int H, int Dk, int Dv, int C);
 hipError_t launch_prefill_f32(const PrefillArgs &a);

@@ -17,6 +17,7 @@
 //
 // This path is exact to fp32 rounding and simple; it is the io_dtype=f32
 // path of the library. The bf16 path (prefill_mfma.hip) is the fast one.
+#include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -45,25 +46,6 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
     for (int n = lo; n < hi; ++n) { chunk_off[n] = run; run += (cu[n + 1] - cu[n] + C - 1) / C; }
 }
 
-struct SeqView {
-    const int32_t *cu;        // nullptr => dense
-    const int32_t *chunk_off; // valid when cu != nullptr
-    int N, T, C;
-    __device__ int total_chunks() const { return cu ? chunk_off[N] : N * ((T + C - 1) / C); }
-    __device__ int seq_start(int n) const { return cu ? cu[n] : n * T; }
-    __device__ int seq_end(int n) const { return cu ? cu[n + 1] : (n + 1) * T; }
-    __device__ int first_chunk(int n) const { return cu ? chunk_off[n] : n * ((T + C - 1) / C); }
-    // sequence holding global chunk ci (ci < total_chunks)
-    __device__ int seq_of_chunk(int ci) const {
-        if (!cu) return ci / ((T + C - 1) / C);
-        int lo = 0, hi = N - 1;   // largest n with chunk_off[n] <= ci and a non-empty range
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (chunk_off[mid] <= ci) lo = mid; else hi = mid - 1;
-        }
-        return lo;
-    }
-};
 
 // Per (chunk, head) record of fp32 operands in the workspace.
 template <int C, int D>
@@ -229,8 +211,8 @@ hipError_t run(const PrefillArgs &a) {
     float *recs = reinterpret_cast<float *>(ws + ((sizeof(int32_t) * (a.N + 1) + 255) / 256) * 256);
     SeqView sv{a.cu_seqlens, chunk_off, a.N, a.T, C};
     if (a.cu_seqlens) {
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.N, C, chunk_off);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        const hipError_t e = launch_chunk_plan(a.cu_seqlens, a.N, C, chunk_off, a.stream);
+        if (e != hipSuccess) return e;
     }
     if (maxc > 0) {
         hipLaunchKernelGGL((prep_kernel<C, D, TI, TB>), dim3((unsigned)maxc, a.H), dim3(256), 0, a.stream,
@@ -259,6 +241,11 @@ hipError_t run_d(const PrefillArgs &a) {
 }
 
 }  // namespace
+
+hipError_t launch_chunk_plan(const int32_t *cu, int N, int C, int32_t *chunk_off, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, C, chunk_off);
+    return hipGetLastError();
+}
 
 size_t prefill_f32_workspace(int N, long long T_total, int H, int Dk, int Dv, int C) {
     (void)Dv;

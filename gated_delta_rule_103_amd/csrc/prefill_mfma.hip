@@ -1,10 +1,809 @@
-// prefill_mfma.hip -- bf16 MFMA chunked prefill (in progress).
+// prefill_mfma.hip -- chunked KDA prefill on MFMA (gfx950): a prep kernel
+// and a scan kernel.
+//
+// Method: the chunk unrolling of the Kimi K3 explainer's FlashKDA paragraph
+// (Q_decay, K_restore, causal M_qk, UT transform for the pseudo-values U).
+// With a = in-chunk cumulative log-decay, gamma = exp(a_last):
+//     Kd = k * exp(a),  Qd = q * exp(a),  Kr = k * exp(a_last - a)
+//     Mqk[t,s] = sum_c q_t k_s exp(a_t - a_s)   (s <= t)
+//     L[t,s]   = beta_t sum_c k_t k_s exp(a_t - a_s)   (s < t)
+//     IB       = (I + L)^{-1} Diag(beta)
+// and per chunk of one (sequence, head), with the state M = S^T:
+//     U     = IB (V - Kd M)
+//     O     = Qd M + Mqk U
+//     M_out = Diag(gamma) M + Kr^T U
+//
+// prep  (one workgroup per (chunk, head), all chunks in parallel): decays
+//       as products of alpha = exp(g) inside 16-token blocks, L and Mqk on
+//       bf16 MFMA with hi/lo split operands, the unit-lower-triangular
+//       inverse by blocked substitution (fp32 MFMA off the diagonal), and a
+//       record of the scan's left operands in fp16, laid out as MFMA
+//       fragments so that the scan loads them with 16-byte coalesced reads.
+// scan  (one workgroup per (sequence, head, 16-column value tile), its chunks
+//       in order): the fp32 state tile stays in registers; five fp16 MFMA
+//       contractions per chunk with the right operand (state, V - Kd M, U)
+//       split into fp16 hi + lo and fp32 accumulation.
+//
+// Every decay factor that is formed is <= 1, except on the diagonal 16x16
+// blocks of L and Mqk, which use the block's own start as reference: their
+// factors exp(-(a_s - a_start)) are bounded by 1 / (whole-block decay) and a
+// block whose decay leaves the fp32 normal range takes an exact per-element
+// path instead.
+#include <algorithm>
+
+#include "kda_chunks.h"
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
-size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C) {
-    return prefill_f32_workspace(N, T_total, H, Dk, Dv, C);
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;       // Dk == Dv
+constexpr int C = 64;        // chunk length
+constexpr int NTHR = 256;    // 4 wavefronts, one per SIMD
+constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-hipError_t launch_prefill_mfma(const PrefillArgs &a) { return launch_prefill_f32(a); }
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 lds8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ f16x8 lds8h(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ float bf2f(__bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ float ld_scalar(const T *p, size_t i);
+template <> __device__ __forceinline__ float ld_scalar<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_scalar<bf16_t>(const bf16_t *p, size_t i) {
+    return bf16_to_f32(p[i]);
+}
+template <typename T> __device__ __forceinline__ void st_scalar(T *p, size_t i, float x);
+template <> __device__ __forceinline__ void st_scalar<float>(float *p, size_t i, float x) { p[i] = x; }
+template <> __device__ __forceinline__ void st_scalar<bf16_t>(bf16_t *p, size_t i, float x) {
+    p[i] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
+}
+
+// x = hi + lo, hi = bf16(x), lo = bf16(x - hi): about 16 significant bits
+#define SPLIT2(x, HI, LO)                                   \
+    do {                                                    \
+        const float x_ = (x);                               \
+        const __bf16 h_ = static_cast<__bf16>(x_);          \
+        (HI) = h_;                                          \
+        (LO) = static_cast<__bf16>(x_ - bf2f(h_));          \
+    } while (0)
+// the same in fp16: about 22 significant bits (|x| < 65504)
+#define SPLITH(x, HI, LO)                                   \
+    do {                                                    \
+        const float x_ = (x);                               \
+        const _Float16 h_ = static_cast<_Float16>(x_);      \
+        (HI) = h_;                                          \
+        (LO) = static_cast<_Float16>(x_ - static_cast<float>(h_)); \
+    } while (0)
+
+// ---------------------------------------------------------------- record
+// Per (chunk, head): for each wavefront role w (tokens 16w..16w+15 and
+// channels 32w..32w+31) 16 KB of fp16 fragments [operand][k-step][lane][8],
+// then d_t = q_t . k_t (fp32 [64]) and gamma (fp32 [128]).
+struct Rec {
+    static constexpr int WAVE = 16384;
+    static constexpr int KD = 0, QD = 4096, IB = 8192, MQ = 10240, KR = 12288;
+    static constexpr int DG = 4 * WAVE, GAM = DG + C * 4, BYTES = GAM + D * 4;
+};
+
+// ---------------------------------------------------------------- prep
+constexpr int SQ = D + 8;        // bf16 row stride of q, k           [64][136]
+constexpr int SE = D + 4;        // fp32 row stride of the decays     [64][132]
+constexpr int SL = C + 4;        // fp32 row stride of L / INV^T      [64][68]
+constexpr int SMQ = C + 8;       // bf16 row stride of Mqk hi / lo    [64][72]
+
+struct PrepLds {
+    static constexpr int Q = 0;
+    static constexpr int K = Q + C * SQ * 2;
+    static constexpr int E = K + C * SQ * 2;         // fp32 in-block prefix decay
+    static constexpr int F = E + C * SE * 4;         // fp32 in-block suffix decay
+    static constexpr int LI = F + C * SE * 4;        // fp32 L (strictly lower) and INV^T (upper, with diagonal)
+    static constexpr int MQK = LI + C * SL * 4;      // bf16 Mqk high part (strictly lower)
+    static constexpr int MQKL = MQK + C * SMQ * 2;   // bf16 Mqk low part
+    static constexpr int DG = MQKL + C * SMQ * 2;    // fp32 [64]
+    static constexpr int BETA = DG + C * 4;          // fp32 [64]
+    static constexpr int GB = BETA + C * 4;          // fp32 [4][128] block decays
+    static constexpr int G = GB + 4 * D * 4;         // fp32 [4][128] decay chunk start -> block start
+    static constexpr int H = G + 4 * D * 4;          // fp32 [4][128] decay block end -> chunk end
+    static constexpr int GAM = H + 4 * D * 4;        // fp32 [128]
+    static constexpr int FLAG = GAM + D * 4;         // int [4]
+    static constexpr int T3 = FLAG + 16;             // fp32 [3][256] inverse scratch
+    static constexpr int SIZE = T3 + 3 * 256 * 4;
+};
+
+struct PrepParams {
+    const bf16_t *q, *k;
+    const float *g;
+    const void *beta;
+    SeqView sv;
+    int H;
+    char *rec;
+};
+
+template <typename TB>
+__global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using Lo = PrepLds;
+    static_assert(Lo::SIZE <= 163840, "LDS budget");
+    __bf16 *sQ = reinterpret_cast<__bf16 *>(smem + Lo::Q);
+    __bf16 *sK = reinterpret_cast<__bf16 *>(smem + Lo::K);
+    float *sE = reinterpret_cast<float *>(smem + Lo::E);
+    float *sF = reinterpret_cast<float *>(smem + Lo::F);
+    float *sLI = reinterpret_cast<float *>(smem + Lo::LI);
+    __bf16 *sMqk = reinterpret_cast<__bf16 *>(smem + Lo::MQK);
+    __bf16 *sMqkL = reinterpret_cast<__bf16 *>(smem + Lo::MQKL);
+    float *sDg = reinterpret_cast<float *>(smem + Lo::DG);
+    float *sBeta = reinterpret_cast<float *>(smem + Lo::BETA);
+    float *sGB = reinterpret_cast<float *>(smem + Lo::GB);
+    float *sG = reinterpret_cast<float *>(smem + Lo::G);
+    float *sH = reinterpret_cast<float *>(smem + Lo::H);
+    float *sGam = reinterpret_cast<float *>(smem + Lo::GAM);
+    int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
+    float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int H = p.H;
+    const int items = p.sv.total_chunks() * H;
+    // inputs of one (chunk, head) item, fetched one item ahead. The loads are
+    // issued unmasked (rows past the end read the last row) and masked when staged,
+    // so nothing waits on them until the next item starts.
+    u32x4 rq[4], rk[4];
+    f32x4 rg[8];
+    TB rbeta = TB(0);          // raw value: converted when staged
+    int nx_h = 0, nx_tok0 = 0, nx_Lc = 0;
+    auto fetch = [&](int item) {
+        const int ci = item / H, h = item % H;
+        const int n = p.sv.seq_of_chunk(ci);
+        const int tok0 = p.sv.seq_start(n) + (ci - p.sv.first_chunk(n)) * C;
+        const int Lc = min(C, p.sv.seq_end(n) - tok0);
+        nx_h = h;
+        nx_tok0 = tok0;
+        nx_Lc = Lc;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = tid + it * NTHR, row = idx >> 4, part = idx & 15;
+            const size_t off = ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 8 * part;
+            rq[it] = *reinterpret_cast<const u32x4 *>(p.q + off);
+            rk[it] = *reinterpret_cast<const u32x4 *>(p.k + off);
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int idx = tid + it * NTHR, row = idx >> 5, part = idx & 31;
+            rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
+        }
+        rbeta = static_cast<const TB *>(p.beta)[(size_t)(tok0 + min(tid, Lc - 1)) * H + h];
+    };
+    if ((int)blockIdx.x < items) fetch(blockIdx.x);
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int ci = item / H, h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
+
+    // ================= stage the chunk in LDS (rows past the end: zeros, alpha = 1)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = tid + it * NTHR, row = idx >> 4, part = idx & 15;
+        const u32x4 z0 = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(sQ + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
+        *reinterpret_cast<u32x4 *>(sK + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int idx = tid + it * NTHR, row = idx >> 5, part = idx & 31;
+        f32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = row < Lc ? __expf(rg[it][e]) : 1.f;
+        *reinterpret_cast<f32x4 *>(sE + row * SE + 4 * part) = a;
+    }
+    if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
+    if (tid < 4) sFlag[tid] = 0;
+    fetch(min(item + (int)gridDim.x, items - 1));   // unconditional: see the scan's prefetch
+    __syncthreads();
+
+        // in-block suffix (F) and prefix (E) products of alpha; thread = (block, channel) x 2
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int pi = tid + it * NTHR, I = pi >> 7, c = pi & 127;
+            float al[16];
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) al[tt] = sE[(16 * I + tt) * SE + c];
+            float f = 1.f;
+#pragma unroll
+            for (int tt = 15; tt >= 0; --tt) {
+                sF[(16 * I + tt) * SE + c] = f;
+                f *= al[tt];
+            }
+            float e = 1.f;
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                e *= al[tt];
+                sE[(16 * I + tt) * SE + c] = e;
+            }
+            sGB[I * D + c] = e;
+            if (!(e >= kTiny)) atomicOr(&sFlag[I], 1);
+        }
+        // exact diagonal d_t = q_t . k_t (4 lanes per row, 32 channels each)
+        {
+            const int row = tid >> 2, seg = tid & 3;
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 qa = lds8(sQ + row * SQ + 32 * seg + 8 * j);
+                const bf16x8 ka = lds8(sK + row * SQ + 32 * seg + 8 * j);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += bf2f(qa[e]) * bf2f(ka[e]);
+            }
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            if (seg == 0) sDg[row] = acc;
+        }
+        __syncthreads();
+        if (tid < D) {
+            const int c = tid;
+            const float g0 = sGB[c], g1 = sGB[D + c], g2 = sGB[2 * D + c], g3 = sGB[3 * D + c];
+            sG[c] = 1.f; sG[D + c] = g0; sG[2 * D + c] = g0 * g1; sG[3 * D + c] = g0 * g1 * g2;
+            sH[3 * D + c] = 1.f; sH[2 * D + c] = g3; sH[D + c] = g2 * g3; sH[c] = g1 * g2 * g3;
+            sGam[c] = g0 * g1 * g2 * g3;
+        }
+        // zero the upper blocks of Mqk (never written below)
+        for (int idx = tid; idx < 6 * 256; idx += NTHR) {
+            const int bb = idx >> 8, e = idx & 255;
+            int I, J;
+            if (bb < 3) { I = bb; J = bb + 1; } else if (bb < 5) { I = bb - 3; J = I + 2; } else { I = 0; J = 3; }
+            sMqk[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<__bf16>(0.f);
+            sMqkL[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<__bf16>(0.f);
+        }
+        __syncthreads();
+
+        // ================= L and Mqk on MFMA, 10 16x16 blocks (I >= J) ========
+        // wave 0: (0,0) (1,0) (3,0); wave 1: (1,1) (2,1) (2,0); wave 2: (2,2) (3,2); wave 3: (3,3) (3,1)
+        {
+            const int nblk = wave < 2 ? 3 : 2;
+            for (int q3 = 0; q3 < nblk; ++q3) {
+                int I, J;
+                if (q3 == 0) { I = wave; J = wave; }
+                else if (q3 == 1) { if (wave == 0) { I = 1; J = 0; } else if (wave == 1) { I = 2; J = 1; }
+                                    else if (wave == 2) { I = 3; J = 2; } else { I = 3; J = 1; } }
+                else { if (wave == 0) { I = 3; J = 0; } else { I = 2; J = 0; } }
+                const bool diag = (I == J);
+                if (diag && sFlag[I]) continue;          // exact path below
+                f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
+                const int t = 16 * I + l16, s = 16 * J + l16, rref = 16 * I + 7;
+#pragma unroll 2
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int c0 = 32 * ks + 8 * lq;
+                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0), sv = lds8(sK + s * SQ + c0);
+                    const f32x4 et0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                    const f32x4 et1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    f32x4 fa0, fa1, fb0, fb1;
+                    if (diag) {
+                        const f32x4 er0 = *reinterpret_cast<const f32x4 *>(sE + rref * SE + c0);
+                        const f32x4 er1 = *reinterpret_cast<const f32x4 *>(sE + rref * SE + c0 + 4);
+                        const f32x4 es0 = *reinterpret_cast<const f32x4 *>(sE + s * SE + c0);
+                        const f32x4 es1 = *reinterpret_cast<const f32x4 *>(sE + s * SE + c0 + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            fa0[e] = et0[e] * __builtin_amdgcn_rcpf(er0[e]);
+                            fa1[e] = et1[e] * __builtin_amdgcn_rcpf(er1[e]);
+                            fb0[e] = er0[e] * __builtin_amdgcn_rcpf(es0[e]);
+                            fb1[e] = er1[e] * __builtin_amdgcn_rcpf(es1[e]);
+                        }
+                    } else {
+                        fa0 = et0;
+                        fa1 = et1;
+                        fb0 = *reinterpret_cast<const f32x4 *>(sF + s * SE + c0);
+                        fb1 = *reinterpret_cast<const f32x4 *>(sF + s * SE + c0 + 4);
+                        for (int K2 = J + 1; K2 < I; ++K2) {
+                            fb0 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0);
+                            fb1 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0 + 4);
+                        }
+                    }
+                    bf16x8 aqh, aql, akh, akl, bkh, bkl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float fa = e < 4 ? fa0[e] : fa1[e - 4], fb = e < 4 ? fb0[e] : fb1[e - 4];
+                        SPLIT2(bf2f(qv[e]) * fa, aqh[e], aql[e]);
+                        SPLIT2(bf2f(kv[e]) * fa, akh[e], akl[e]);
+                        SPLIT2(bf2f(sv[e]) * fb, bkh[e], bkl[e]);
+                    }
+                    accL = mfma_bf16(akh, bkh, accL);
+                    accM = mfma_bf16(aqh, bkh, accM);
+                    accL = mfma_bf16(akh, bkl, accL);
+                    accM = mfma_bf16(aqh, bkl, accM);
+                    accL = mfma_bf16(akl, bkh, accL);
+                    accM = mfma_bf16(aql, bkh, accM);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tr = 16 * I + 4 * lq + i, sc = 16 * J + l16;
+                    const bool lower = sc < tr;
+                    if (lower || !diag) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
+                    __bf16 mh, ml;
+                    SPLIT2(lower ? accM[i] : 0.f, mh, ml);
+                    sMqk[tr * SMQ + sc] = mh;
+                    sMqkL[tr * SMQ + sc] = ml;
+                }
+            }
+        }
+        // exact path for diagonal blocks whose in-block decay leaves the fp32 normal range
+        for (int I = 0; I < 4; ++I) {
+            if (!sFlag[I]) continue;                     // uniform across the workgroup
+            if (wave == I) {
+                for (int tr = 1; tr < 16; ++tr)
+                    for (int sc = 0; sc < tr; ++sc) {
+                        const int T_ = 16 * I + tr, S_ = 16 * I + sc;
+                        float accl = 0.f, accm = 0.f;
+                        for (int c = lane; c < D; c += 64) {
+                            float lg = 0.f;
+                            for (int rho = S_ + 1; rho <= T_; ++rho)
+                                lg += (rho < Lc) ? p.g[((size_t)(tok0 + rho) * H + h) * D + c] : 0.f;
+                            const float w = expf(lg), kk = bf2f(sK[S_ * SQ + c]);
+                            accl += bf2f(sK[T_ * SQ + c]) * kk * w;
+                            accm += bf2f(sQ[T_ * SQ + c]) * kk * w;
+                        }
+                        accl = warp_sum(accl);
+                        accm = warp_sum(accm);
+                        if (lane == 0) {
+                            sLI[T_ * SL + S_] = sBeta[T_] * accl;
+                            __bf16 mh, ml;
+                            SPLIT2(accm, mh, ml);
+                            sMqk[T_ * SMQ + S_] = mh;
+                            sMqkL[T_ * SMQ + S_] = ml;
+                        }
+                    }
+                for (int e = lane; e < 256; e += 64)
+                    if ((e & 15) >= (e >> 4)) {
+                        sMqk[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<__bf16>(0.f);
+                        sMqkL[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<__bf16>(0.f);
+                    }
+            }
+        }
+        __syncthreads();
+
+        // ================= INV = (I + L)^{-1}, stored transposed in the upper triangle
+        // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II
+        if (lane < 16) {
+            const int I = wave, col = lane;
+            float x[16];
+#pragma unroll
+            for (int tr = 0; tr < 16; ++tr) {
+                float v = (tr == col) ? 1.f : 0.f;
+#pragma unroll
+                for (int sc = 0; sc < tr; ++sc) v -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
+                x[tr] = (tr < col) ? 0.f : v;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int tr = 0; tr < 16; ++tr)
+                if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
+        }
+        __syncthreads();
+        // off-diagonal blocks, one level (I - J) at a time, on fp32 MFMA (exact products):
+        //   T = sum_{K=J}^{I-1} L_IK INV_KJ ;  INV_IJ = -INV_II T
+        // INV_XY[a][b] lives at sLI[(16Y + b) * SL + 16X + a]; for X == Y only a >= b is stored.
+        for (int lev = 1; lev < 4; ++lev) {
+            if (wave < 4 - lev) {
+                const int J = wave, I = J + lev;
+                const int row = l16, kk = lq;          // 16x16x4 fragment: lane -> (row/col, k)
+                f32x4 T4 = {0.f, 0.f, 0.f, 0.f};
+                for (int K2 = J; K2 < I; ++K2) {
+#pragma unroll
+                    for (int sl = 0; sl < 4; ++sl) {
+                        const int k = 4 * sl + kk;
+                        const float a = sLI[(16 * I + row) * SL + 16 * K2 + k];                  // L_IK[row][k]
+                        const float bv = (K2 == J && k < row) ? 0.f : sLI[(16 * J + row) * SL + 16 * K2 + k];  // INV_KJ[k][col=row]
+                        T4 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, T4, 0, 0, 0);
+                    }
+                }
+                // T (lane: col l16, rows 4lq..4lq+3) -> scratch [row][col] for the B operand
+                float *tw = sT3 + wave * 256;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tw[(4 * lq + i) * 16 + l16] = T4[i];
+                __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): scratch written before it is read
+                f32x4 O4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) {
+                    const int k = 4 * sl + kk;
+                    const float a = (row >= k) ? sLI[(16 * I + k) * SL + 16 * I + row] : 0.f;   // INV_II[row][k]
+                    const float bv = tw[k * 16 + l16];                                           // T[k][col]
+                    O4 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, O4, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -O4[i];
+            }
+            __syncthreads();
+        }
+
+
+    // ================= record: fp16 fragments of the scan's left operands
+    {
+        char *rec = p.rec + ((size_t)ci * H + h) * Rec::BYTES + (size_t)wave * Rec::WAVE;
+        const int t = 16 * wave + l16, I = wave;
+        // Kd, Qd: row t, k-step ks covers channels 32ks + 8lq .. +7
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 32 * ks + 8 * lq;
+            const bf16x8 kx = lds8(sK + t * SQ + c0), qx = lds8(sQ + t * SQ + c0);
+            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0);
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0 + 4);
+            f16x8 kd, qd;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
+                kd[e] = static_cast<_Float16>(bf2f(kx[e]) * dec);
+                qd[e] = static_cast<_Float16>(bf2f(qx[e]) * dec);
+            }
+            *reinterpret_cast<f16x8 *>(rec + Rec::KD + ks * 1024 + lane * 16) = kd;
+            *reinterpret_cast<f16x8 *>(rec + Rec::QD + ks * 1024 + lane * 16) = qd;
+        }
+        // IB = INV Diag(beta) and Mqk: row t, k-step ks covers tokens 32ks + 8lq .. +7
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f16x8 ib, mq;
+            const bf16x8 mh = lds8(sMqk + t * SMQ + 32 * ks + 8 * lq);
+            const bf16x8 ml = lds8(sMqkL + t * SMQ + 32 * ks + 8 * lq);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sc = 32 * ks + 8 * lq + e;
+                // INV[t][sc] is stored at (sc, t); zero for sc > t
+                const float x = (sc <= t) ? sLI[sc * SL + t] * sBeta[sc] : 0.f;
+                ib[e] = static_cast<_Float16>(x);
+                mq[e] = static_cast<_Float16>(bf2f(mh[e]) + bf2f(ml[e]));
+            }
+            *reinterpret_cast<f16x8 *>(rec + Rec::IB + ks * 1024 + lane * 16) = ib;
+            *reinterpret_cast<f16x8 *>(rec + Rec::MQ + ks * 1024 + lane * 16) = mq;
+        }
+        // Kr^T: row = channel 32w + 16rt + l16, k-step ks covers tokens 32ks + 8lq .. +7
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int chn = 32 * wave + 16 * rt + l16;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f16x8 kr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tt = 32 * ks + 8 * lq + e;
+                    kr[e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] * sH[(tt >> 4) * D + chn]);
+                }
+                *reinterpret_cast<f16x8 *>(rec + Rec::KR + (rt * 2 + ks) * 1024 + lane * 16) = kr;
+            }
+        }
+        char *tail = p.rec + ((size_t)ci * H + h) * Rec::BYTES;
+        if (tid < C) reinterpret_cast<float *>(tail + Rec::DG)[tid] = sDg[tid];
+        if (tid < D) reinterpret_cast<float *>(tail + Rec::GAM)[tid] = sGam[tid];
+    }
+    __syncthreads();      // LDS is restaged by the next item
+    }
+}
+
+// ---------------------------------------------------------------- scan
+constexpr int SMS = D + 8;       // fp16 row stride of the state       [col][136]
+constexpr int SYU = C + 8;       // fp16 row stride of Y and U         [col][72]
+
+template <int TV>
+struct ScanLds {
+    static constexpr int M = 0;                      // fp16 [2][TV][SMS] state hi / lo, [col][channel]
+    static constexpr int Y = M + 2 * TV * SMS * 2;   // fp16 [2][TV][SYU] (V - Kd M) hi / lo, [col][token]
+    static constexpr int U = Y + 2 * TV * SYU * 2;   // fp16 [2][TV][SYU] U hi / lo, [col][token]
+    static constexpr int SIZE = U + 2 * TV * SYU * 2;
+};
+
+struct ScanParams {
+    const bf16_t *v;
+    const float *S0;
+    void *out;
+    float *S_out;
+    SeqView sv;
+    int H, chains;
+    const char *rec;
+};
+
+template <int TV, typename TO>
+__global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using Lo = ScanLds<TV>;
+    constexpr int NT = TV / 16;
+    constexpr int TEAM = D / TV;
+    _Float16 *sMh = reinterpret_cast<_Float16 *>(smem + Lo::M);
+    _Float16 *sMl = sMh + TV * SMS;
+    _Float16 *sYh = reinterpret_cast<_Float16 *>(smem + Lo::Y);
+    _Float16 *sYl = sYh + TV * SYU;
+    _Float16 *sUh = reinterpret_cast<_Float16 *>(smem + Lo::U);
+    _Float16 *sUl = sUh + TV * SYU;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    // XCD-aware placement: block b runs on XCD b % 8; the TEAM workgroups of
+    // one chain share b % 8 and so one L2, where the chain's records are read.
+    const int b = blockIdx.x;
+    const int xcd = b & 7, r = b >> 3;
+    const int member = r % TEAM, grp = r / TEAM;
+    const int chain = grp * 8 + xcd;
+    if (chain >= p.chains) return;
+    const int H = p.H, n = chain / H, h = chain % H;
+    const int col0 = member * TV;
+    const int start = p.sv.seq_start(n), end = p.sv.seq_end(n);
+    const int nch = (end - start + C - 1) / C, c0 = p.sv.first_chunk(n);
+    const size_t st_off = ((size_t)n * H + h) * D * D;
+    const int tb = 16 * wave;
+
+    // state tile: wave w owns channels 32w..32w+31 (two 16-row tiles)
+    f32x4 Macc[2][NT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int chn = 32 * wave + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                Macc[rt][nt][i] = p.S0 ? p.S0[st_off + (size_t)chn * D + col] : 0.f;
+            }
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f16x4 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) SPLITH(Macc[rt][nt][i], hi[i], lo[i]);
+                const int col = 16 * nt + l16, chn = 32 * wave + 16 * rt + 4 * lq;
+                *reinterpret_cast<f16x4 *>(sMh + col * SMS + chn) = hi;
+                *reinterpret_cast<f16x4 *>(sMl + col * SMS + chn) = lo;
+            }
+    };
+    publish_state();
+    __syncthreads();
+
+    // operands of one chunk, loaded one chunk ahead
+    struct Frags {
+        f16x8 kd[4], qd[4], ib[2], mq[2], kr[2][2];
+        f32x4 dg, gam[2];
+        uint32_t v[NT][4];        // the 32-bit word holding the bf16 value; unpacked where used,
+                                  // so no instruction right after the load waits for it
+    };
+    auto load = [&](int j, Frags &f) {
+        const char *rec = p.rec + ((size_t)(c0 + j) * H + h) * Rec::BYTES;
+        const char *rw = rec + (size_t)wave * Rec::WAVE + lane * 16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            f.kd[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::KD + ks * 1024);
+            f.qd[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::QD + ks * 1024);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f.ib[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::IB + ks * 1024);
+            f.mq[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::MQ + ks * 1024);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                f.kr[rt][ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::KR + (rt * 2 + ks) * 1024);
+        // d for rows tb + 4lq .. +3 and gamma for channels 32w + 16rt + 4lq .. +3: one
+        // 16-byte load each (few load instructions keep two chunks within vmcnt's range)
+        f.dg = *reinterpret_cast<const f32x4 *>(rec + Rec::DG + (tb + 4 * lq) * 4);
+        f.gam[0] = *reinterpret_cast<const f32x4 *>(rec + Rec::GAM + (32 * wave + 4 * lq) * 4);
+        f.gam[1] = *reinterpret_cast<const f32x4 *>(rec + Rec::GAM + (32 * wave + 16 + 4 * lq) * 4);
+        // rows past the end of the sequence read the last row: their values never
+        // matter, because beta = 0 there makes the matching rows and columns of IB
+        // zero. No select right after the load, so nothing waits on loads in flight.
+        const int tok0 = start + j * C, Lc = min(C, end - tok0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tc = min(tb + 4 * lq + i, Lc - 1);
+                const size_t e = ((size_t)(tok0 + tc) * H + h) * D + col0 + 16 * nt + l16;
+                f.v[nt][i] = reinterpret_cast<const uint32_t *>(p.v)[e >> 1];
+            }
+    };
+
+    // Three operand buffers, used round-robin without copies: the loads for a chunk
+    // are issued two chunks before it is consumed.
+    auto step = [&](const Frags &f, int j) {
+        const int tok0 = start + j * C, Lc = min(C, end - tok0);
+
+        // X = Kd M and O = Qd M for tokens tb..tb+15 (state split hi + lo)
+        f32x4 accX[NT], accO[NT], Ureg[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accO[nt] = accX[nt];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
+                const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
+                accX[nt] = mfma_f16(f.kd[ks], bh, accX[nt]);
+                accO[nt] = mfma_f16(f.qd[ks], bh, accO[nt]);
+                accX[nt] = mfma_f16(f.kd[ks], bl, accX[nt]);
+                accO[nt] = mfma_f16(f.qd[ks], bl, accO[nt]);
+            }
+            f16x4 hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // element parity = l16 parity (row offsets and col0 are even)
+                const uint32_t w = f.v[nt][i];
+                const float vv = __uint_as_float((l16 & 1) ? (w & 0xffff0000u) : (w << 16));
+                SPLITH(vv - accX[nt][i], hi[i], lo[i]);
+            }
+            const int col = 16 * nt + l16, t = tb + 4 * lq;
+            *reinterpret_cast<f16x4 *>(sYh + col * SYU + t) = hi;
+            *reinterpret_cast<f16x4 *>(sYl + col * SYU + t) = lo;
+        }
+        __syncthreads();
+        // U = IB Y (Y split hi + lo)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 bh = lds8h(sYh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+                const f16x8 bl = lds8h(sYl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+                u = mfma_f16(f.ib[ks], bh, u);
+                u = mfma_f16(f.ib[ks], bl, u);
+            }
+            Ureg[nt] = u;
+            f16x4 hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) SPLITH(u[i], hi[i], lo[i]);
+            const int col = 16 * nt + l16, t = tb + 4 * lq;
+            *reinterpret_cast<f16x4 *>(sUh + col * SYU + t) = hi;
+            *reinterpret_cast<f16x4 *>(sUl + col * SYU + t) = lo;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            // M = Diag(gamma) M + Kr^T U for channels 32w..32w+31
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[rt][nt][i] *= f.gam[rt][i];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 bh = lds8h(sUh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+                const f16x8 bl = lds8h(sUl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bh, Macc[rt][nt]);
+                    Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bl, Macc[rt][nt]);
+                }
+                // O += Mqk (strictly lower) U
+                accO[nt] = mfma_f16(f.mq[ks], bh, accO[nt]);
+                accO[nt] = mfma_f16(f.mq[ks], bl, accO[nt]);
+            }
+            // + diag(q.k) U with U in fp32, then store
+            const int col = col0 + 16 * nt + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb + 4 * lq + i;
+                const float o = accO[nt][i] + f.dg[i] * Ureg[nt][i];
+                if (t < Lc) st_scalar<TO>(static_cast<TO *>(p.out), ((size_t)(tok0 + t) * H + h) * D + col, o);
+            }
+        }
+        publish_state();
+        __syncthreads();
+    };
+    // The prefetches are unconditional (the chunk index is clamped, so the tail
+    // re-reads the last record): conditional loads would make every later wait
+    // on vector memory conservative and defeat the prefetch.
+    Frags A, B, Cb;
+    if (nch > 0) {
+        const int last = nch - 1;
+        load(0, A);
+        load(min(1, last), B);
+        for (int j = 0; j < nch; j += 3) {
+            load(min(j + 2, last), Cb);
+            step(A, j);
+            if (j + 1 >= nch) break;
+            load(min(j + 3, last), A);
+            step(B, j + 1);
+            if (j + 2 >= nch) break;
+            load(min(j + 4, last), B);
+            step(Cb, j + 2);
+        }
+    }
+
+    if (p.S_out) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int chn = 32 * wave + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                    p.S_out[st_off + (size_t)chn * D + col] = Macc[rt][nt][i];
+                }
+    }
+}
+
+// ---------------------------------------------------------------- host
+constexpr int kTV = 16;
+// persistent prep: one workgroup per compute unit (its LDS use allows one)
+long long prep_grid() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+size_t ws_head(int N) { return ((sizeof(int32_t) * (size_t)(N + 1) + 255) / 256) * 256; }
+
+template <typename TB, typename TO>
+hipError_t run(const PrefillArgs &a) {
+    char *ws = static_cast<char *>(a.ws);
+    int32_t *chunk_off = reinterpret_cast<int32_t *>(ws);
+    char *recs = ws + ws_head(a.N);
+    SeqView sv{a.cu_seqlens, chunk_off, a.N, a.T, C};
+    if (a.cu_seqlens) {
+        const hipError_t e = launch_chunk_plan(a.cu_seqlens, a.N, C, chunk_off, a.stream);
+        if (e != hipSuccess) return e;
+    }
+    const long long maxc = max_chunks(a.N, (long long)a.B * a.T, C);
+    {
+        auto kern = chunk_prep_kernel<TB>;
+        static bool attr = false;
+        if (!attr) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
+            if (e != hipSuccess) return e;
+            attr = true;
+        }
+        PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, a.H, recs};
+        // persistent: a few workgroups per CU walk the (chunk, head) items
+        const long long items = maxc * a.H;
+        const unsigned grid = (unsigned)std::min<long long>(items, prep_grid());
+        if (items > 0) {
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), PrepLds::SIZE, a.stream, pp);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    {
+        constexpr int TEAM = D / kTV;
+        auto kern = chunk_scan_kernel<kTV, TO>;
+        const int chains = a.N * a.H;
+        const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * TEAM;
+        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs};
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(NTHR), ScanLds<kTV>::SIZE, a.stream, sp);
+        return hipGetLastError();
+    }
+}
+
+template <typename TB>
+hipError_t run_o(const PrefillArgs &a) {
+    return a.out_dt == Dt::F32 ? run<TB, float>(a) : run<TB, bf16_t>(a);
+}
+
+}  // namespace
+
+size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C_) {
+    if (Dk == D && Dv == D && C_ == C)
+        return ws_head(N) + (size_t)max_chunks(N, T_total, C) * H * Rec::BYTES;
+    return prefill_f32_workspace(N, T_total, H, Dk, Dv, C_);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs &a) {
+    // The MFMA kernels cover Dk = Dv = 128 with C = 64; other supported
+    // shapes run the fp32-arithmetic kernels on the same bf16 inputs.
+    if (a.Dk == D && a.C == C) return a.beta_dt == Dt::F32 ? run_o<float>(a) : run_o<bf16_t>(a);
+    return launch_prefill_f32(a);
+}
+
 }  // namespace kda

@@ -59,7 +59,8 @@ def _prefill(lib, **kw):
     (dict(cu=ctypes.c_void_p(512), B=2, N=2), -1),
     (dict(Dk=96, Dv=96), -2), (dict(Dk=64, Dv=128), -2), (dict(C=8), -2), (dict(C=128), -2),
     (dict(io=0, bd=1, od=0), -2), (dict(io=0, bd=0, od=1), -2),
-    (dict(ws=None, wsb=0), -3),
+    (dict(ws=None, wsb=0, io=0, bd=0, od=0), -3),
+    (dict(q=ctypes.c_void_p(264)), -1), (dict(g=ctypes.c_void_p(260)), -1),
     (dict(ws=ctypes.c_void_p(256), wsb=16), -3),
 ])
 def test_prefill_argument_errors(lib, kw, status):
@@ -70,11 +71,13 @@ def test_prefill_workspace_misaligned(lib):
     need = lib.kda_prefill_workspace_size(1, 64, 2, 64, 64, 16, 1)
     assert need > 0
     assert _prefill(lib, ws=ctypes.c_void_p(4096 + 64), wsb=need) == -3
+    # the bf16 MFMA configuration (Dk = Dv = 128, C = 64) keeps one record per (chunk, head)
+    assert lib.kda_prefill_workspace_size(1, 8192, 32, 128, 128, 64, 1) >= 129 * 32 * 65536
 
 
 def test_workspace_size_is_pure_and_rejects_bad_sizes(lib):
-    a = lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 1)
-    assert a == lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 1)
+    a = lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 0)
+    assert a > 0 and a == lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 0)
     assert lib.kda_prefill_workspace_size(0, 100, 2, 64, 64, 16, 1) == 0
     assert lib.kda_prefill_workspace_size(1, 100, 2, 96, 96, 16, 1) == 0
     assert lib.kda_prefill_workspace_size(1, 100, 2, 64, 64, 12, 1) == 0
