@@ -26,7 +26,7 @@
 //
 // Every decay factor that is formed is <= 1, except on the diagonal 16x16
 // blocks of L and Mqk, which use the block's own start as reference: their
-// factors exp(-(a_s - a_start)) are bounded by 1 / (whole-block decay) and a
+// factors exp(a_start - a_s) are bounded by 1 / (whole-block decay), and a
 // block whose decay leaves the fp32 normal range takes an exact per-element
 // path instead.
 #include <algorithm>
@@ -97,10 +97,11 @@ struct Rec {
 };
 
 // ---------------------------------------------------------------- prep
+constexpr int PTHR = 512;        // prep: 8 wavefronts, two per SIMD to hide latency
 constexpr int SQ = D + 8;        // bf16 row stride of q, k           [64][136]
 constexpr int SE = D + 4;        // fp32 row stride of the decays     [64][132]
 constexpr int SL = C + 4;        // fp32 row stride of L / INV^T      [64][68]
-constexpr int SMQ = C + 8;       // bf16 row stride of Mqk hi / lo    [64][72]
+constexpr int SMQ = C + 8;       // fp16 row stride of Mqk            [64][72]
 
 struct PrepLds {
     static constexpr int Q = 0;
@@ -108,9 +109,8 @@ struct PrepLds {
     static constexpr int E = K + C * SQ * 2;         // fp32 in-block prefix decay
     static constexpr int F = E + C * SE * 4;         // fp32 in-block suffix decay
     static constexpr int LI = F + C * SE * 4;        // fp32 L (strictly lower) and INV^T (upper, with diagonal)
-    static constexpr int MQK = LI + C * SL * 4;      // bf16 Mqk high part (strictly lower)
-    static constexpr int MQKL = MQK + C * SMQ * 2;   // bf16 Mqk low part
-    static constexpr int DG = MQKL + C * SMQ * 2;    // fp32 [64]
+    static constexpr int MQK = LI + C * SL * 4;      // fp16 strictly lower Mqk
+    static constexpr int DG = MQK + C * SMQ * 2;     // fp32 [64]
     static constexpr int BETA = DG + C * 4;          // fp32 [64]
     static constexpr int GB = BETA + C * 4;          // fp32 [4][128] block decays
     static constexpr int G = GB + 4 * D * 4;         // fp32 [4][128] decay chunk start -> block start
@@ -131,7 +131,7 @@ struct PrepParams {
 };
 
 template <typename TB>
-__global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
     static_assert(Lo::SIZE <= 163840, "LDS budget");
@@ -140,8 +140,7 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
     float *sE = reinterpret_cast<float *>(smem + Lo::E);
     float *sF = reinterpret_cast<float *>(smem + Lo::F);
     float *sLI = reinterpret_cast<float *>(smem + Lo::LI);
-    __bf16 *sMqk = reinterpret_cast<__bf16 *>(smem + Lo::MQK);
-    __bf16 *sMqkL = reinterpret_cast<__bf16 *>(smem + Lo::MQKL);
+    _Float16 *sMqk = reinterpret_cast<_Float16 *>(smem + Lo::MQK);
     float *sDg = reinterpret_cast<float *>(smem + Lo::DG);
     float *sBeta = reinterpret_cast<float *>(smem + Lo::BETA);
     float *sGB = reinterpret_cast<float *>(smem + Lo::GB);
@@ -151,16 +150,18 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
     float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lq = lane >> 4;
+    const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // 8 wavefronts
     const int H = p.H;
     const int items = p.sv.total_chunks() * H;
-    // inputs of one (chunk, head) item, fetched one item ahead. The loads are
-    // issued unmasked (rows past the end read the last row) and masked when staged,
-    // so nothing waits on them until the next item starts.
-    u32x4 rq[4], rk[4];
-    f32x4 rg[8];
-    TB rbeta = TB(0);          // raw value: converted when staged
+
+    // Inputs of one (chunk, head) item, fetched one item ahead. The loads are
+    // issued unmasked (rows past the end read the last row) and masked when
+    // staged, and the next fetch is unconditional (clamped item index): a load
+    // that is used right away or issued under a branch makes the compiler wait
+    // for every load in flight.
+    u32x4 rq[2], rk[2];
+    f32x4 rg[4];
+    TB rbeta = TB(0);
     int nx_h = 0, nx_tok0 = 0, nx_Lc = 0;
     auto fetch = [&](int item) {
         const int ci = item / H, h = item % H;
@@ -171,48 +172,52 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
         nx_tok0 = tok0;
         nx_Lc = Lc;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid + it * NTHR, row = idx >> 4, part = idx & 15;
+        for (int it = 0; it < 2; ++it) {
+            const int idx = tid0 + it * PTHR, row = idx >> 4, part = idx & 15;
             const size_t off = ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 8 * part;
             rq[it] = *reinterpret_cast<const u32x4 *>(p.q + off);
             rk[it] = *reinterpret_cast<const u32x4 *>(p.k + off);
         }
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int idx = tid + it * NTHR, row = idx >> 5, part = idx & 31;
+        for (int it = 0; it < 4; ++it) {
+            const int idx = tid0 + it * PTHR, row = idx >> 5, part = idx & 31;
             rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
         }
-        rbeta = static_cast<const TB *>(p.beta)[(size_t)(tok0 + min(tid, Lc - 1)) * H + h];
+        rbeta = static_cast<const TB *>(p.beta)[(size_t)(tok0 + min(tid0 & 63, Lc - 1)) * H + h];
     };
     if ((int)blockIdx.x < items) fetch(blockIdx.x);
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int ci = item / H, h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
+        const int ci = item / H, h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
+        // per-thread LDS addresses are recomputed every item instead of being
+        // hoisted out of the loop and held in registers for its whole length
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
 
-    // ================= stage the chunk in LDS (rows past the end: zeros, alpha = 1)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int idx = tid + it * NTHR, row = idx >> 4, part = idx & 15;
-        const u32x4 z0 = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(sQ + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
-        *reinterpret_cast<u32x4 *>(sK + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int idx = tid + it * NTHR, row = idx >> 5, part = idx & 31;
-        f32x4 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = row < Lc ? __expf(rg[it][e]) : 1.f;
-        *reinterpret_cast<f32x4 *>(sE + row * SE + 4 * part) = a;
-    }
-    if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
-    if (tid < 4) sFlag[tid] = 0;
-    fetch(min(item + (int)gridDim.x, items - 1));   // unconditional: see the scan's prefetch
-    __syncthreads();
-
-        // in-block suffix (F) and prefix (E) products of alpha; thread = (block, channel) x 2
+        // ================= stage the chunk in LDS (rows past the end: zeros, alpha = 1)
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int pi = tid + it * NTHR, I = pi >> 7, c = pi & 127;
+            const int idx = tid + it * PTHR, row = idx >> 4, part = idx & 15;
+            const u32x4 z0 = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(sQ + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
+            *reinterpret_cast<u32x4 *>(sK + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = tid + it * PTHR, row = idx >> 5, part = idx & 31;
+            f32x4 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = row < Lc ? __expf(rg[it][e]) : 1.f;
+            *reinterpret_cast<f32x4 *>(sE + row * SE + 4 * part) = a;
+        }
+        if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
+        if (tid < 4) sFlag[tid] = 0;
+        fetch(min(item + (int)gridDim.x, items - 1));
+        __syncthreads();
+
+        // ================= in-block suffix (F) and prefix (E) products of alpha
+        {
+            const int I = tid >> 7, c = tid & 127;          // one (block, channel) per thread
             float al[16];
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt) al[tt] = sE[(16 * I + tt) * SE + c];
@@ -231,20 +236,25 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
             sGB[I * D + c] = e;
             if (!(e >= kTiny)) atomicOr(&sFlag[I], 1);
         }
-        // exact diagonal d_t = q_t . k_t (4 lanes per row, 32 channels each)
+        // exact diagonal d_t = q_t . k_t (8 lanes per row, 16 channels each)
         {
-            const int row = tid >> 2, seg = tid & 3;
+            const int row = tid >> 3, seg = tid & 7;
+            const bf16x8 qa = lds8(sQ + row * SQ + 16 * seg), qb = lds8(sQ + row * SQ + 16 * seg + 8);
+            const bf16x8 ka = lds8(sK + row * SQ + 16 * seg), kb = lds8(sK + row * SQ + 16 * seg + 8);
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 qa = lds8(sQ + row * SQ + 32 * seg + 8 * j);
-                const bf16x8 ka = lds8(sK + row * SQ + 32 * seg + 8 * j);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc += bf2f(qa[e]) * bf2f(ka[e]);
-            }
+            for (int e = 0; e < 8; ++e) acc += bf2f(qa[e]) * bf2f(ka[e]) + bf2f(qb[e]) * bf2f(kb[e]);
             acc += __shfl_xor(acc, 1, 64);
             acc += __shfl_xor(acc, 2, 64);
+            acc += __shfl_xor(acc, 4, 64);
             if (seg == 0) sDg[row] = acc;
+        }
+        // zero the upper blocks of Mqk (never written below)
+        for (int idx = tid; idx < 6 * 256; idx += PTHR) {
+            const int bb = idx >> 8, e = idx & 255;
+            int I, J;
+            if (bb < 3) { I = bb; J = bb + 1; } else if (bb < 5) { I = bb - 3; J = I + 2; } else { I = 0; J = 3; }
+            sMqk[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<_Float16>(0.f);
         }
         __syncthreads();
         if (tid < D) {
@@ -254,83 +264,87 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
             sH[3 * D + c] = 1.f; sH[2 * D + c] = g3; sH[D + c] = g2 * g3; sH[c] = g1 * g2 * g3;
             sGam[c] = g0 * g1 * g2 * g3;
         }
-        // zero the upper blocks of Mqk (never written below)
-        for (int idx = tid; idx < 6 * 256; idx += NTHR) {
-            const int bb = idx >> 8, e = idx & 255;
-            int I, J;
-            if (bb < 3) { I = bb; J = bb + 1; } else if (bb < 5) { I = bb - 3; J = I + 2; } else { I = 0; J = 3; }
-            sMqk[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<__bf16>(0.f);
-            sMqkL[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<__bf16>(0.f);
-        }
-        __syncthreads();
 
-        // ================= L and Mqk on MFMA, 10 16x16 blocks (I >= J) ========
-        // wave 0: (0,0) (1,0) (3,0); wave 1: (1,1) (2,1) (2,0); wave 2: (2,2) (3,2); wave 3: (3,3) (3,1)
-        {
-            const int nblk = wave < 2 ? 3 : 2;
-            for (int q3 = 0; q3 < nblk; ++q3) {
-                int I, J;
-                if (q3 == 0) { I = wave; J = wave; }
-                else if (q3 == 1) { if (wave == 0) { I = 1; J = 0; } else if (wave == 1) { I = 2; J = 1; }
-                                    else if (wave == 2) { I = 3; J = 2; } else { I = 3; J = 1; } }
-                else { if (wave == 0) { I = 3; J = 0; } else { I = 2; J = 0; } }
-                const bool diag = (I == J);
-                if (diag && sFlag[I]) continue;          // exact path below
-                f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
-                const int t = 16 * I + l16, s = 16 * J + l16, rref = 16 * I + 7;
-#pragma unroll 2
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int c0 = 32 * ks + 8 * lq;
-                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0), sv = lds8(sK + s * SQ + c0);
-                    const f32x4 et0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                    const f32x4 et1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-                    f32x4 fa0, fa1, fb0, fb1;
-                    if (diag) {
-                        const f32x4 er0 = *reinterpret_cast<const f32x4 *>(sE + rref * SE + c0);
-                        const f32x4 er1 = *reinterpret_cast<const f32x4 *>(sE + rref * SE + c0 + 4);
-                        const f32x4 es0 = *reinterpret_cast<const f32x4 *>(sE + s * SE + c0);
-                        const f32x4 es1 = *reinterpret_cast<const f32x4 *>(sE + s * SE + c0 + 4);
+        // ================= L and Mqk on MFMA, the 10 16x16 blocks with I >= J ==
+        // wave -> (block-row I, blocks J0..J1): 0:(3,0-1) 1:(3,2-3) 2:(2,0-1) 3:(2,2)
+        // 4:(1,0-1) 5:(0,0). The row's left operands x_t * E_t (x = q or k) are built
+        // once per k-step for the wave's blocks. Right operands:
+        //   J < I : k_s * F_s * prod_{J<K<I} Gamma_K   (every factor <= 1)
+        //   J = I : k_s / E_s                          (start of block as reference,
+        //           bounded by 1 / Gamma_I; a block with Gamma_I below FLT_MIN takes
+        //           the exact path instead)
+        // Operands are split into bf16 hi + lo (three products per k-step).
+        if (wave < 6) {
+            const int I = wave < 2 ? 3 : wave < 4 ? 2 : wave == 4 ? 1 : 0;
+            const int J0 = (wave == 1) ? 2 : (wave == 3) ? 2 : 0;
+            const int J1 = (wave == 0 || wave == 2 || wave == 4) ? J0 + 1 : J0 + (wave == 1 ? 1 : 0);
+            const bool diag_ok = !sFlag[I];
+            const int t = 16 * I + l16;
+            f32x4 accL[2], accM[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) { accL[jj] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[jj] = accL[jj]; }
+#pragma unroll 1
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 32 * ks + 8 * lq;
+                const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
+                const f32x4 et0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                const f32x4 et1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                bf16x8 aqh, aql, akh, akl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float fa = e < 4 ? et0[e] : et1[e - 4];
+                    SPLIT2(bf2f(qv[e]) * fa, aqh[e], aql[e]);
+                    SPLIT2(bf2f(kv[e]) * fa, akh[e], akl[e]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int J = J0 + jj;
+                    if (J > J1 || (J == I && !diag_ok)) continue;
+                    const int sr = 16 * J + l16;
+                    const bf16x8 sv = lds8(sK + sr * SQ + c0);
+                    f32x4 fb0, fb1;
+                    if (J == I) {
+                        const f32x4 es0 = *reinterpret_cast<const f32x4 *>(sE + sr * SE + c0);
+                        const f32x4 es1 = *reinterpret_cast<const f32x4 *>(sE + sr * SE + c0 + 4);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            fa0[e] = et0[e] * __builtin_amdgcn_rcpf(er0[e]);
-                            fa1[e] = et1[e] * __builtin_amdgcn_rcpf(er1[e]);
-                            fb0[e] = er0[e] * __builtin_amdgcn_rcpf(es0[e]);
-                            fb1[e] = er1[e] * __builtin_amdgcn_rcpf(es1[e]);
+                            fb0[e] = __builtin_amdgcn_rcpf(es0[e]);
+                            fb1[e] = __builtin_amdgcn_rcpf(es1[e]);
                         }
                     } else {
-                        fa0 = et0;
-                        fa1 = et1;
-                        fb0 = *reinterpret_cast<const f32x4 *>(sF + s * SE + c0);
-                        fb1 = *reinterpret_cast<const f32x4 *>(sF + s * SE + c0 + 4);
+                        fb0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
+                        fb1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
                         for (int K2 = J + 1; K2 < I; ++K2) {
                             fb0 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0);
                             fb1 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0 + 4);
                         }
                     }
-                    bf16x8 aqh, aql, akh, akl, bkh, bkl;
+                    bf16x8 bkh, bkl;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float fa = e < 4 ? fa0[e] : fa1[e - 4], fb = e < 4 ? fb0[e] : fb1[e - 4];
-                        SPLIT2(bf2f(qv[e]) * fa, aqh[e], aql[e]);
-                        SPLIT2(bf2f(kv[e]) * fa, akh[e], akl[e]);
+                        const float fb = e < 4 ? fb0[e] : fb1[e - 4];
                         SPLIT2(bf2f(sv[e]) * fb, bkh[e], bkl[e]);
                     }
-                    accL = mfma_bf16(akh, bkh, accL);
-                    accM = mfma_bf16(aqh, bkh, accM);
-                    accL = mfma_bf16(akh, bkl, accL);
-                    accM = mfma_bf16(aqh, bkl, accM);
-                    accL = mfma_bf16(akl, bkh, accL);
-                    accM = mfma_bf16(aql, bkh, accM);
+                    accL[jj] = mfma_bf16(akh, bkh, accL[jj]);
+                    accM[jj] = mfma_bf16(aqh, bkh, accM[jj]);
+                    accL[jj] = mfma_bf16(akh, bkl, accL[jj]);
+                    accM[jj] = mfma_bf16(aqh, bkl, accM[jj]);
+                    accL[jj] = mfma_bf16(akl, bkh, accL[jj]);
+                    accM[jj] = mfma_bf16(aql, bkh, accM[jj]);
                 }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int J = J0 + jj;
+                const bool diag = (J == I);
+                if (J > J1 || (diag && !diag_ok)) continue;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = 16 * I + 4 * lq + i, sc = 16 * J + l16;
                     const bool lower = sc < tr;
-                    if (lower || !diag) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
-                    __bf16 mh, ml;
-                    SPLIT2(lower ? accM[i] : 0.f, mh, ml);
-                    sMqk[tr * SMQ + sc] = mh;
-                    sMqkL[tr * SMQ + sc] = ml;
+                    // masked entries of a diagonal block may hold inf / nan: select, do not scale
+                    if (lower || !diag) sLI[tr * SL + sc] = sBeta[tr] * accL[jj][i];
+                    sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[jj][i] : 0.f);
                 }
             }
         }
@@ -354,24 +368,18 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
                         accm = warp_sum(accm);
                         if (lane == 0) {
                             sLI[T_ * SL + S_] = sBeta[T_] * accl;
-                            __bf16 mh, ml;
-                            SPLIT2(accm, mh, ml);
-                            sMqk[T_ * SMQ + S_] = mh;
-                            sMqkL[T_ * SMQ + S_] = ml;
+                            sMqk[T_ * SMQ + S_] = static_cast<_Float16>(accm);
                         }
                     }
                 for (int e = lane; e < 256; e += 64)
-                    if ((e & 15) >= (e >> 4)) {
-                        sMqk[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<__bf16>(0.f);
-                        sMqkL[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<__bf16>(0.f);
-                    }
+                    if ((e & 15) >= (e >> 4)) sMqk[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<_Float16>(0.f);
             }
         }
         __syncthreads();
 
         // ================= INV = (I + L)^{-1}, stored transposed in the upper triangle
         // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II
-        if (lane < 16) {
+        if (wave < 4 && lane < 16) {
             const int I = wave, col = lane;
             float x[16];
 #pragma unroll
@@ -423,67 +431,67 @@ __global__ __launch_bounds__(NTHR) void chunk_prep_kernel(PrepParams p) {
             __syncthreads();
         }
 
-
-    // ================= record: fp16 fragments of the scan's left operands
-    {
-        char *rec = p.rec + ((size_t)ci * H + h) * Rec::BYTES + (size_t)wave * Rec::WAVE;
-        const int t = 16 * wave + l16, I = wave;
-        // Kd, Qd: row t, k-step ks covers channels 32ks + 8lq .. +7
+        // ================= record: fp16 fragments of the scan's left operands
+        // waves 0-3: tokens 16w..16w+15 (Kd, Qd, IB, Mqk); waves 4-7: channels
+        // 32(w-4)..+31 (Kr^T). Record role r = wave & 3.
+        {
+            const int role = wave & 3;
+            char *rec = p.rec + ((size_t)ci * H + h) * Rec::BYTES + (size_t)role * Rec::WAVE;
+            if (wave < 4) {
+                const int t = 16 * role + l16, I = role;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int c0 = 32 * ks + 8 * lq;
-            const bf16x8 kx = lds8(sK + t * SQ + c0), qx = lds8(sQ + t * SQ + c0);
-            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0);
-            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0 + 4);
-            f16x8 kd, qd;
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int c0 = 32 * ks + 8 * lq;
+                    const bf16x8 kx = lds8(sK + t * SQ + c0), qx = lds8(sQ + t * SQ + c0);
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0 + 4);
+                    f16x8 kd, qd;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
-                kd[e] = static_cast<_Float16>(bf2f(kx[e]) * dec);
-                qd[e] = static_cast<_Float16>(bf2f(qx[e]) * dec);
-            }
-            *reinterpret_cast<f16x8 *>(rec + Rec::KD + ks * 1024 + lane * 16) = kd;
-            *reinterpret_cast<f16x8 *>(rec + Rec::QD + ks * 1024 + lane * 16) = qd;
-        }
-        // IB = INV Diag(beta) and Mqk: row t, k-step ks covers tokens 32ks + 8lq .. +7
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            f16x8 ib, mq;
-            const bf16x8 mh = lds8(sMqk + t * SMQ + 32 * ks + 8 * lq);
-            const bf16x8 ml = lds8(sMqkL + t * SMQ + 32 * ks + 8 * lq);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sc = 32 * ks + 8 * lq + e;
-                // INV[t][sc] is stored at (sc, t); zero for sc > t
-                const float x = (sc <= t) ? sLI[sc * SL + t] * sBeta[sc] : 0.f;
-                ib[e] = static_cast<_Float16>(x);
-                mq[e] = static_cast<_Float16>(bf2f(mh[e]) + bf2f(ml[e]));
-            }
-            *reinterpret_cast<f16x8 *>(rec + Rec::IB + ks * 1024 + lane * 16) = ib;
-            *reinterpret_cast<f16x8 *>(rec + Rec::MQ + ks * 1024 + lane * 16) = mq;
-        }
-        // Kr^T: row = channel 32w + 16rt + l16, k-step ks covers tokens 32ks + 8lq .. +7
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int chn = 32 * wave + 16 * rt + l16;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                f16x8 kr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tt = 32 * ks + 8 * lq + e;
-                    kr[e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] * sH[(tt >> 4) * D + chn]);
+                    for (int e = 0; e < 8; ++e) {
+                        const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
+                        kd[e] = static_cast<_Float16>(bf2f(kx[e]) * dec);
+                        qd[e] = static_cast<_Float16>(bf2f(qx[e]) * dec);
+                    }
+                    *reinterpret_cast<f16x8 *>(rec + Rec::KD + ks * 1024 + lane * 16) = kd;
+                    *reinterpret_cast<f16x8 *>(rec + Rec::QD + ks * 1024 + lane * 16) = qd;
                 }
-                *reinterpret_cast<f16x8 *>(rec + Rec::KR + (rt * 2 + ks) * 1024 + lane * 16) = kr;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    f16x8 ib;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int sc = 32 * ks + 8 * lq + e;
+                        // INV[t][sc] is stored at (sc, t); zero for sc > t
+                        const float x = (sc <= t) ? sLI[sc * SL + t] * sBeta[sc] : 0.f;
+                        ib[e] = static_cast<_Float16>(x);
+                    }
+                    *reinterpret_cast<f16x8 *>(rec + Rec::IB + ks * 1024 + lane * 16) = ib;
+                    *reinterpret_cast<f16x8 *>(rec + Rec::MQ + ks * 1024 + lane * 16) =
+                        *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
+                }
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int chn = 32 * role + 16 * rt + l16;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        f16x8 kr;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int tt = 32 * ks + 8 * lq + e;
+                            kr[e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] * sH[(tt >> 4) * D + chn]);
+                        }
+                        *reinterpret_cast<f16x8 *>(rec + Rec::KR + (rt * 2 + ks) * 1024 + lane * 16) = kr;
+                    }
+                }
             }
+            char *tail = p.rec + ((size_t)ci * H + h) * Rec::BYTES;
+            if (tid < C) reinterpret_cast<float *>(tail + Rec::DG)[tid] = sDg[tid];
+            if (tid < D) reinterpret_cast<float *>(tail + Rec::GAM)[tid] = sGam[tid];
         }
-        char *tail = p.rec + ((size_t)ci * H + h) * Rec::BYTES;
-        if (tid < C) reinterpret_cast<float *>(tail + Rec::DG)[tid] = sDg[tid];
-        if (tid < D) reinterpret_cast<float *>(tail + Rec::GAM)[tid] = sGam[tid];
-    }
-    __syncthreads();      // LDS is restaged by the next item
+        __syncthreads();      // LDS is restaged by the next item
     }
 }
 
@@ -770,7 +778,7 @@ hipError_t run(const PrefillArgs &a) {
         const long long items = maxc * a.H;
         const unsigned grid = (unsigned)std::min<long long>(items, prep_grid());
         if (items > 0) {
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), PrepLds::SIZE, a.stream, pp);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(PTHR), PrepLds::SIZE, a.stream, pp);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
