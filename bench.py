@@ -93,20 +93,46 @@ def bench_decode(steps, warmup):
                 frac_hbm=state_bytes / (ms_step * 1e-3) / 1e9 / costs.MI355X_PEAK["hbm_GBps"])
 
 
-def cpu_baseline(p):
-    """The fp64 oracle on the whole single-sequence workload (32 heads x 8192 tokens)."""
+def cpu_baseline(p, min_seconds=10.0):
+    """The fp64 oracle on the whole single-sequence workload (32 heads x 8192
+    tokens), repeated until about `min_seconds` of host time has been spent."""
     import oracle
     H = p.q.shape[2]
     f64 = lambda t: t.detach().cpu().double().numpy().reshape(-1, H, t.shape[-1])
     q, k, v, g = (f64(t) for t in (p.q, p.k, p.v, p.g))
     beta = p.beta.detach().cpu().double().numpy().reshape(-1, H)
     threads = oracle.default_threads(H)
-    t0 = time.perf_counter()
-    oracle.recurrent(q, k, v, g, beta, nthreads=threads)
-    dt = time.perf_counter() - t0
-    return dict(value=q.shape[0] / dt / 1e6, unit="Mtok/s", cores=threads, kind="oracle",
-                sample=f"whole {PREFILL_WORKLOAD} workload: {H} heads x {q.shape[0]} tokens, fp64, "
-                       f"{dt:.2f} s wall")
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrent(q, k, v, g, beta, nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return dict(value=q.shape[0] * reps / dt / 1e6, unit="Mtok/s", cores=threads, kind="oracle",
+                sample=f"whole {PREFILL_WORKLOAD} workload ({H} heads x {q.shape[0]} tokens, fp64 "
+                       f"per-token recurrence) run {reps} times, {dt:.1f} s wall")
+
+
+def measured_traffic(unit, workload):
+    """HBM bytes per launch recorded under profiles/ from rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (already scaled by the copy-probe calibration), or None when
+    the kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) != 7 or cells[0] != "traffic" or cells[1] != unit or cells[2] != workload:
+                continue
+            src = os.path.join(ROOT, cells[3])
+            if not os.path.exists(src):
+                return None
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            if not sha.startswith(cells[4]):
+                return None
+            return int(cells[5]) + int(cells[6])
+    return None
 
 
 def main():
@@ -116,6 +142,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the bench, run a plain device copy of MIB MiB three times "
+                         "(the known-size reference that scales HBM counter readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the KDA hot path runs on a single MI355X); "
@@ -151,8 +180,10 @@ def main():
                    "Dk": w["D"], "Dv": w["D"], "C": w["C"], "io": "bf16 q/k/v/o/beta, fp32 g/state",
                    "gate": "-softplus(N(0,1)+2)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak_tf, 4), "traffic": None,
-                     "kernel": "kda_prefill (whole call)", "model": "12C^3+8C^2D+6CD^2 per chunk-head",
+                     "unit": "TFLOP/s", "frac": round(tflops / peak_tf, 4),
+                     "traffic": measured_traffic("kda_prefill", PREFILL_WORKLOAD),
+                     "kernel": "kda_prefill call (chunk_prep_kernel + chunk_scan_kernel)",
+                     "model": "12C^3+8C^2D+6CD^2 FLOP per chunk-head",
                      "kernel_ms": round(pf["kernel_ms"], 4)},
         "roofline_hbm": {"bound": "hbm", "achieved": round(gbps, 1), "peak": peak_bw, "unit": "GB/s",
                          "frac": round(gbps / peak_bw, 4),
@@ -162,12 +193,25 @@ def main():
         line["decode"] = {"workload": DECODE_WORKLOAD, "ms_per_token_step": round(dec["ms_per_token_step"], 4),
                           "roofline": {"bound": "hbm", "achieved": round(dec["gbps_state"], 1),
                                        "peak": peak_bw, "unit": "GB/s",
-                                       "frac": round(dec["frac_hbm"], 4), "traffic": None,
+                                       "frac": round(dec["frac_hbm"], 4),
+                                       "traffic": measured_traffic("kda_decode", DECODE_WORKLOAD),
                                        "model": "8*D^2 bytes per head-step"},
                           "gbps_incl_vectors": round(dec["gbps_total"], 1)}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe)
+
+
+def copy_probe(mib):
+    """A plain elementwise copy of `mib` MiB (reads mib MiB, writes mib MiB per launch)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
