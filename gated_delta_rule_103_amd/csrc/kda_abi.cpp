@@ -58,8 +58,9 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g, con
     if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
     const long long T_total = (long long)B * T;
     if (T_total > INT_MAX / 2 || (long long)N * H > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
-    // q, k and g are read with 16-byte vector loads
-    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(g)) & 15u)
+    // q, k, v and g are read with 16-byte vector loads
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+         reinterpret_cast<uintptr_t>(g)) & 15u)
         return KDA_ERR_INVALID_ARG;
     if (!head_dims_supported(Dk, Dv) || !chunk_supported(C)) return KDA_ERR_UNSUPPORTED;
     if (io_dtype == KDA_F32 && (beta_dtype != KDA_F32 || out_dtype != KDA_F32)) return KDA_ERR_UNSUPPORTED;

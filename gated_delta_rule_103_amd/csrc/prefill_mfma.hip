@@ -48,6 +48,24 @@ constexpr int C = 64;        // chunk length
 constexpr int NTHR = 256;    // 4 wavefronts, one per SIMD
 constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 
+// Which right-hand operands of the scan's fp16 contractions are split into
+// hi + lo (two MFMAs) rather than rounded once
+#ifndef KDA_SPLIT_X
+#define KDA_SPLIT_X 1     // the state in X = Kd M
+#endif
+#ifndef KDA_SPLIT_OI
+#define KDA_SPLIT_OI 1    // the state in O = Qd M
+#endif
+#ifndef KDA_SPLIT_Y
+#define KDA_SPLIT_Y 1     // V - X in U = IB (V - X)
+#endif
+#ifndef KDA_SPLIT_U
+#define KDA_SPLIT_U 1     // U in M += Kr^T U
+#endif
+#ifndef KDA_SPLIT_UO
+#define KDA_SPLIT_UO 1    // U in O += Mqk U
+#endif
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -89,7 +107,9 @@ template <> __device__ __forceinline__ void st_scalar<bf16_t>(bf16_t *p, size_t 
 // ---------------------------------------------------------------- record
 // Per (chunk, head): for each wavefront role w (tokens 16w..16w+15 and
 // channels 32w..32w+31) 16 KB of fp16 fragments [operand][k-step][lane][8],
-// then d_t = q_t . k_t (fp32 [64]) and gamma (fp32 [128]).
+// then d_t = q_t . k_t (fp32 [64]) and gamma (fp32 [128]). Records are
+// stored head-major (index head * records-per-head + chunk), so the records a
+// scan chain walks through are contiguous in memory.
 struct Rec {
     static constexpr int WAVE = 16384;
     static constexpr int KD = 0, QD = 4096, IB = 8192, MQ = 10240, KR = 12288;
@@ -128,6 +148,7 @@ struct PrepParams {
     SeqView sv;
     int H;
     char *rec;
+    long long rec_stride;        // records per head (head-major record layout)
 };
 
 template <typename TB>
@@ -436,7 +457,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // 32(w-4)..+31 (Kr^T). Record role r = wave & 3.
         {
             const int role = wave & 3;
-            char *rec = p.rec + ((size_t)ci * H + h) * Rec::BYTES + (size_t)role * Rec::WAVE;
+            char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES + (size_t)role * Rec::WAVE;
             if (wave < 4) {
                 const int t = 16 * role + l16, I = role;
 #pragma unroll
@@ -487,7 +508,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     }
                 }
             }
-            char *tail = p.rec + ((size_t)ci * H + h) * Rec::BYTES;
+            char *tail = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES;
             if (tid < C) reinterpret_cast<float *>(tail + Rec::DG)[tid] = sDg[tid];
             if (tid < D) reinterpret_cast<float *>(tail + Rec::GAM)[tid] = sGam[tid];
         }
@@ -515,6 +536,7 @@ struct ScanParams {
     SeqView sv;
     int H, chains;
     const char *rec;
+    long long rec_stride;        // records per head
 };
 
 template <int TV, typename TO>
@@ -581,7 +603,7 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                                   // so no instruction right after the load waits for it
     };
     auto load = [&](int j, Frags &f) {
-        const char *rec = p.rec + ((size_t)(c0 + j) * H + h) * Rec::BYTES;
+        const char *rec = p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES;
         const char *rw = rec + (size_t)wave * Rec::WAVE + lane * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -634,8 +656,12 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                 const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
                 accX[nt] = mfma_f16(f.kd[ks], bh, accX[nt]);
                 accO[nt] = mfma_f16(f.qd[ks], bh, accO[nt]);
+#if KDA_SPLIT_X
                 accX[nt] = mfma_f16(f.kd[ks], bl, accX[nt]);
+#endif
+#if KDA_SPLIT_OI
                 accO[nt] = mfma_f16(f.qd[ks], bl, accO[nt]);
+#endif
             }
             f16x4 hi, lo;
 #pragma unroll
@@ -659,7 +685,9 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                 const f16x8 bh = lds8h(sYh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
                 const f16x8 bl = lds8h(sYl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
                 u = mfma_f16(f.ib[ks], bh, u);
+#if KDA_SPLIT_Y
                 u = mfma_f16(f.ib[ks], bl, u);
+#endif
             }
             Ureg[nt] = u;
             f16x4 hi, lo;
@@ -684,11 +712,15 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bh, Macc[rt][nt]);
+#if KDA_SPLIT_U
                     Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bl, Macc[rt][nt]);
+#endif
                 }
                 // O += Mqk (strictly lower) U
                 accO[nt] = mfma_f16(f.mq[ks], bh, accO[nt]);
+#if KDA_SPLIT_UO
                 accO[nt] = mfma_f16(f.mq[ks], bl, accO[nt]);
+#endif
             }
             // + diag(q.k) U with U in fp32, then store
             const int col = col0 + 16 * nt + l16;
@@ -773,7 +805,7 @@ hipError_t run(const PrefillArgs &a) {
             if (e != hipSuccess) return e;
             attr = true;
         }
-        PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, a.H, recs};
+        PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, a.H, recs, maxc};
         // persistent: a few workgroups per CU walk the (chunk, head) items
         const long long items = maxc * a.H;
         const unsigned grid = (unsigned)std::min<long long>(items, prep_grid());
@@ -788,7 +820,7 @@ hipError_t run(const PrefillArgs &a) {
         auto kern = chunk_scan_kernel<kTV, TO>;
         const int chains = a.N * a.H;
         const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * TEAM;
-        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs};
+        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc};
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(NTHR), ScanLds<kTV>::SIZE, a.stream, sp);
         return hipGetLastError();
     }

@@ -22,7 +22,7 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers, dense and contiguous, in the
- *     layouts given below; q, k and g of kda_prefill must be 16-byte
+ *     layouts given below; q, k, v and g of kda_prefill must be 16-byte
  *     aligned. The caller owns every buffer; the library never allocates or
  *     frees device memory and keeps no mutable global state.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null

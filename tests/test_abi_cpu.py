@@ -61,6 +61,7 @@ def _prefill(lib, **kw):
     (dict(io=0, bd=1, od=0), -2), (dict(io=0, bd=0, od=1), -2),
     (dict(ws=None, wsb=0, io=0, bd=0, od=0), -3),
     (dict(q=ctypes.c_void_p(264)), -1), (dict(g=ctypes.c_void_p(260)), -1),
+    (dict(v=ctypes.c_void_p(258)), -1),
     (dict(ws=ctypes.c_void_p(256), wsb=16), -3),
 ])
 def test_prefill_argument_errors(lib, kw, status):
