@@ -286,86 +286,95 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             sGam[c] = g0 * g1 * g2 * g3;
         }
 
-        // ================= L and Mqk on MFMA, the 10 16x16 blocks with I >= J ==
-        // wave -> (block-row I, blocks J0..J1): 0:(3,0-1) 1:(3,2-3) 2:(2,0-1) 3:(2,2)
-        // 4:(1,0-1) 5:(0,0). The row's left operands x_t * E_t (x = q or k) are built
-        // once per k-step for the wave's blocks. Right operands:
-        //   J < I : k_s * F_s * prod_{J<K<I} Gamma_K   (every factor <= 1)
-        //   J = I : k_s / E_s                          (start of block as reference,
-        //           bounded by 1 / Gamma_I; a block with Gamma_I below FLT_MIN takes
-        //           the exact path instead)
-        // Operands are split into bf16 hi + lo (three products per k-step).
-        if (wave < 6) {
-            const int I = wave < 2 ? 3 : wave < 4 ? 2 : wave == 4 ? 1 : 0;
-            const int J0 = (wave == 1) ? 2 : (wave == 3) ? 2 : 0;
-            const int J1 = (wave == 0 || wave == 2 || wave == 4) ? J0 + 1 : J0 + (wave == 1 ? 1 : 0);
-            const bool diag_ok = !sFlag[I];
-            const int t = 16 * I + l16;
+        // ================= L and Mqk on MFMA, the 10 16x16 blocks with I >= J
+        // Left operands x_t E_t (x = k for L, q for Mqk), t in block I.
+        // Diagonal blocks (wavefronts 0-3, I = J = wavefront): right operands k_s / E_s
+        // (start of block as reference, bounded by 1 / Gamma_I; a block with Gamma_I
+        // below FLT_MIN takes the exact path instead), both operands split into bf16
+        // hi + lo (three products per k-step): near-diagonal entries dominate o.
+        // Off-diagonal blocks (wavefronts 4-6, two blocks each): right operands
+        // k_s F_s prod_{J<K<I} Gamma_K; every factor is <= 1, so both operands are
+        // rounded once to fp16 (11-bit significand) and multiplied on fp16 MFMA.
+        //   wavefront 4: (3,0) (3,1)   5: (3,2) (1,0)   6: (2,0) (2,1)
+        if (wave < 4) {
+            const int I = wave;
+            if (!sFlag[I]) {
+                const int t = 16 * I + l16;
+                f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
+#pragma unroll 1
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int c0 = 32 * ks + 8 * lq;
+                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    bf16x8 aqh, aql, akh, akl, bkh, bkl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float ee = e < 4 ? e0[e] : e1[e - 4];
+                        SPLIT2(bf2f(qv[e]) * ee, aqh[e], aql[e]);
+                        SPLIT2(bf2f(kv[e]) * ee, akh[e], akl[e]);
+                        // same rows: the right operand is k_s / E_s
+                        SPLIT2(bf2f(kv[e]) * __builtin_amdgcn_rcpf(ee), bkh[e], bkl[e]);
+                    }
+                    // (lane l16 holds row t as left operand and column s = t as right operand)
+                    accL = mfma_bf16(akh, bkh, accL);
+                    accM = mfma_bf16(aqh, bkh, accM);
+                    accL = mfma_bf16(akh, bkl, accL);
+                    accM = mfma_bf16(aqh, bkl, accM);
+                    accL = mfma_bf16(akl, bkh, accL);
+                    accM = mfma_bf16(aql, bkh, accM);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
+                    const bool lower = sc < tr;
+                    // masked entries may hold inf / nan: select, do not scale
+                    if (lower) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
+                    sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
+                }
+            }
+        } else if (wave < 7) {
+            const int I0 = wave == 6 ? 2 : 3, J0 = wave == 5 ? 2 : 0;
+            const int I1 = wave == 4 ? 3 : (wave == 5 ? 1 : 2), J1 = wave == 5 ? 0 : 1;
             f32x4 accL[2], accM[2];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) { accL[jj] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[jj] = accL[jj]; }
+            for (int bb = 0; bb < 2; ++bb) { accL[bb] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[bb] = accL[bb]; }
 #pragma unroll 1
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 32 * ks + 8 * lq;
-                const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
-                const f32x4 et0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                const f32x4 et1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-                bf16x8 aqh, aql, akh, akl;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float fa = e < 4 ? et0[e] : et1[e - 4];
-                    SPLIT2(bf2f(qv[e]) * fa, aqh[e], aql[e]);
-                    SPLIT2(bf2f(kv[e]) * fa, akh[e], akl[e]);
-                }
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int J = J0 + jj;
-                    if (J > J1 || (J == I && !diag_ok)) continue;
-                    const int sr = 16 * J + l16;
-                    const bf16x8 sv = lds8(sK + sr * SQ + c0);
-                    f32x4 fb0, fb1;
-                    if (J == I) {
-                        const f32x4 es0 = *reinterpret_cast<const f32x4 *>(sE + sr * SE + c0);
-                        const f32x4 es1 = *reinterpret_cast<const f32x4 *>(sE + sr * SE + c0 + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            fb0[e] = __builtin_amdgcn_rcpf(es0[e]);
-                            fb1[e] = __builtin_amdgcn_rcpf(es1[e]);
-                        }
-                    } else {
-                        fb0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
-                        fb1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
-                        for (int K2 = J + 1; K2 < I; ++K2) {
-                            fb0 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0);
-                            fb1 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0 + 4);
-                        }
+                for (int bb = 0; bb < 2; ++bb) {
+                    const int I = bb ? I1 : I0, J = bb ? J1 : J0;
+                    const int t = 16 * I + l16, sr = 16 * J + l16;
+                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0), sv = lds8(sK + sr * SQ + c0);
+                    f32x4 a0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                    f32x4 a1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    f32x4 b0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
+                    f32x4 b1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
+                    for (int K2 = J + 1; K2 < I; ++K2) {
+                        b0 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0);
+                        b1 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0 + 4);
                     }
-                    bf16x8 bkh, bkl;
+                    f16x8 aq, ak, bk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float fb = e < 4 ? fb0[e] : fb1[e - 4];
-                        SPLIT2(bf2f(sv[e]) * fb, bkh[e], bkl[e]);
+                        const float fa = e < 4 ? a0[e] : a1[e - 4], fb = e < 4 ? b0[e] : b1[e - 4];
+                        aq[e] = static_cast<_Float16>(bf2f(qv[e]) * fa);
+                        ak[e] = static_cast<_Float16>(bf2f(kv[e]) * fa);
+                        bk[e] = static_cast<_Float16>(bf2f(sv[e]) * fb);
                     }
-                    accL[jj] = mfma_bf16(akh, bkh, accL[jj]);
-                    accM[jj] = mfma_bf16(aqh, bkh, accM[jj]);
-                    accL[jj] = mfma_bf16(akh, bkl, accL[jj]);
-                    accM[jj] = mfma_bf16(aqh, bkl, accM[jj]);
-                    accL[jj] = mfma_bf16(akl, bkh, accL[jj]);
-                    accM[jj] = mfma_bf16(aql, bkh, accM[jj]);
+                    accL[bb] = mfma_f16(ak, bk, accL[bb]);
+                    accM[bb] = mfma_f16(aq, bk, accM[bb]);
                 }
             }
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int J = J0 + jj;
-                const bool diag = (J == I);
-                if (J > J1 || (diag && !diag_ok)) continue;
+            for (int bb = 0; bb < 2; ++bb) {
+                const int I = bb ? I1 : I0, J = bb ? J1 : J0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = 16 * I + 4 * lq + i, sc = 16 * J + l16;
-                    const bool lower = sc < tr;
-                    // masked entries of a diagonal block may hold inf / nan: select, do not scale
-                    if (lower || !diag) sLI[tr * SL + sc] = sBeta[tr] * accL[jj][i];
-                    sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[jj][i] : 0.f);
+                    sLI[tr * SL + sc] = sBeta[tr] * accL[bb][i];
+                    sMqk[tr * SMQ + sc] = static_cast<_Float16>(accM[bb][i]);
                 }
             }
         }
