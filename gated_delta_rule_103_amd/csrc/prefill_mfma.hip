@@ -146,12 +146,23 @@ struct PrepParams {
     const float *g;
     const void *beta;
     SeqView sv;
+    const int2 *meta;            // packed sequences: {first token, length} of every chunk
     int H;
     char *rec;
     long long rec_stride;        // records per head (head-major record layout)
 };
 
-template <typename TB>
+// {first token, length} of every chunk of packed sequences (zeros past the last)
+__global__ __launch_bounds__(256) void chunk_meta_kernel(SeqView sv, int2 *meta, int maxc) {
+    const int ci = blockIdx.x * 256 + threadIdx.x;
+    if (ci >= maxc) return;
+    if (ci >= sv.total_chunks()) { meta[ci] = int2{0, 0}; return; }
+    const int n = sv.seq_of_chunk(ci);
+    const int tok0 = sv.seq_start(n) + (ci - sv.first_chunk(n)) * C;
+    meta[ci] = int2{tok0, min(C, sv.seq_end(n) - tok0)};
+}
+
+template <typename TB, bool VARLEN>
 __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
@@ -180,15 +191,32 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     // staged, and the next fetch is unconditional (clamped item index): a load
     // that is used right away or issued under a branch makes the compiler wait
     // for every load in flight.
+    // {first token, length} of global chunk ci: arithmetic for dense batches; for
+    // packed sequences from the chunk table, read one fetch ahead so that the
+    // value is never waited for right after its load (such a wait would also
+    // wait for the previous item's record stores)
+    auto dense_meta = [&](int ci) {
+        const int n = ci / p.sv.dense_chunks();
+        const int tok0 = n * p.sv.T + (ci - n * p.sv.dense_chunks()) * C;
+        return int2{tok0, min(C, (n + 1) * p.sv.T - tok0)};
+    };
+    int2 meta_ahead = {0, 0};
+    if constexpr (VARLEN)
+        if ((int)blockIdx.x < items) meta_ahead = p.meta[(int)blockIdx.x / H];
     u32x4 rq[2], rk[2];
     f32x4 rg[4];
     TB rbeta = TB(0);
     int nx_h = 0, nx_tok0 = 0, nx_Lc = 0;
     auto fetch = [&](int item) {
         const int ci = item / H, h = item % H;
-        const int n = p.sv.seq_of_chunk(ci);
-        const int tok0 = p.sv.seq_start(n) + (ci - p.sv.first_chunk(n)) * C;
-        const int Lc = min(C, p.sv.seq_end(n) - tok0);
+        int2 m;
+        if constexpr (VARLEN) {
+            m = meta_ahead;
+            meta_ahead = p.meta[min(item + (int)gridDim.x, items - 1) / H];
+        } else {
+            m = dense_meta(ci);
+        }
+        const int tok0 = m.x, Lc = m.y;
         nx_h = h;
         nx_tok0 = tok0;
         nx_Lc = Lc;
@@ -792,30 +820,39 @@ long long prep_grid() {
     return cus;
 }
 
-size_t ws_head(int N) { return ((sizeof(int32_t) * (size_t)(N + 1) + 255) / 256) * 256; }
+// workspace: chunk offsets (N + 1 int32), the chunk table (maxc int2), records
+size_t ws_offs(int N) { return ((sizeof(int32_t) * (size_t)(N + 1) + 255) / 256) * 256; }
+size_t ws_meta(long long maxc) { return ((sizeof(int2) * (size_t)maxc + 255) / 256) * 256; }
 
 template <typename TB, typename TO>
 hipError_t run(const PrefillArgs &a) {
+    const long long maxc = max_chunks(a.N, (long long)a.B * a.T, C);
     char *ws = static_cast<char *>(a.ws);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws);
-    char *recs = ws + ws_head(a.N);
+    int2 *meta = reinterpret_cast<int2 *>(ws + ws_offs(a.N));
+    char *recs = ws + ws_offs(a.N) + ws_meta(maxc);
     SeqView sv{a.cu_seqlens, chunk_off, a.N, a.T, C};
-    if (a.cu_seqlens) {
-        const hipError_t e = launch_chunk_plan(a.cu_seqlens, a.N, C, chunk_off, a.stream);
+    const bool varlen = a.cu_seqlens != nullptr;
+    if (varlen) {
+        hipError_t e = launch_chunk_plan(a.cu_seqlens, a.N, C, chunk_off, a.stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(chunk_meta_kernel, dim3((unsigned)((maxc + 255) / 256)), dim3(256), 0, a.stream,
+                           sv, meta, (int)maxc);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const long long maxc = max_chunks(a.N, (long long)a.B * a.T, C);
     {
-        auto kern = chunk_prep_kernel<TB>;
-        static bool attr = false;
-        if (!attr) {
+        auto kern = varlen ? chunk_prep_kernel<TB, true> : chunk_prep_kernel<TB, false>;
+        static bool attr[2] = {false, false};
+        if (!attr[varlen]) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
             if (e != hipSuccess) return e;
-            attr = true;
+            attr[varlen] = true;
         }
-        PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, a.H, recs, maxc};
-        // persistent: a few workgroups per CU walk the (chunk, head) items
+        PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, meta,
+                      a.H, recs, maxc};
+        // persistent: one workgroup per CU walks the (chunk, head) items
         const long long items = maxc * a.H;
         const unsigned grid = (unsigned)std::min<long long>(items, prep_grid());
         if (items > 0) {
@@ -844,7 +881,7 @@ hipError_t run_o(const PrefillArgs &a) {
 
 size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C_) {
     if (Dk == D && Dv == D && C_ == C)
-        return ws_head(N) + (size_t)max_chunks(N, T_total, C) * H * Rec::BYTES;
+        return ws_offs(N) + ws_meta(max_chunks(N, T_total, C)) + (size_t)max_chunks(N, T_total, C) * H * Rec::BYTES;
     return prefill_f32_workspace(N, T_total, H, Dk, Dv, C_);
 }
 
