@@ -49,12 +49,14 @@ constexpr int NTHR = 256;    // 4 wavefronts, one per SIMD
 constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 
 // Which right-hand operands of the scan's fp16 contractions are split into
-// hi + lo (two MFMAs) rather than rounded once
+// hi + lo (two MFMAs) rather than rounded once. The state update keeps ~22
+// bits in every operand that feeds back into the state (X, V - X, U); the
+// output-only products round once (11 bits).
 #ifndef KDA_SPLIT_X
 #define KDA_SPLIT_X 1     // the state in X = Kd M
 #endif
 #ifndef KDA_SPLIT_OI
-#define KDA_SPLIT_OI 1    // the state in O = Qd M
+#define KDA_SPLIT_OI 0    // the state in O = Qd M (o only: its error is not fed back)
 #endif
 #ifndef KDA_SPLIT_Y
 #define KDA_SPLIT_Y 1     // V - X in U = IB (V - X)
@@ -63,7 +65,7 @@ constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 #define KDA_SPLIT_U 1     // U in M += Kr^T U
 #endif
 #ifndef KDA_SPLIT_UO
-#define KDA_SPLIT_UO 1    // U in O += Mqk U
+#define KDA_SPLIT_UO 0    // U in O += Mqk U (o only)
 #endif
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
