@@ -6,42 +6,51 @@
 // FLOPs and 8*D^2 bytes per head: the fp32 state is read once and written
 // once, so the kernel is a stream over HBM.
 //
-// Layout of the work: one 256-thread workgroup per (sequence, head) chain.
-// Thread t owns the float4 column group (t mod D/4) of every (256*4/D)-th row,
-// so each wavefront reads whole 512-byte rows (fully coalesced) and the state
-// stays in registers between the read and the write. o is formed from the
-// same pass: o = M'^T q + (q.k) u, so only one reduction round is needed.
+// Layout of the work: the D value columns of one (sequence, head) chain are
+// split over two workgroups (the reductions run over key rows, so column
+// slices are independent). A thread owns one float4 column group of every
+// (NT*4/W)-th row of its slice; each wavefront reads whole 256-byte row
+// slices, and the state stays in registers between the read and the write.
+// o is formed from the same pass: o = M'^T q + (q.k) u, so only one reduction
+// round is needed. The state is read with ordinary loads and written with
+// streaming (non-temporal) stores, which measured fastest.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-template <int D, typename TI, typename TB, typename TO>
-__global__ __launch_bounds__(256) void decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
-                                                     const TI *__restrict__ v, const float *__restrict__ g,
-                                                     const TB *__restrict__ beta, float *__restrict__ S,
-                                                     TO *__restrict__ out) {
-    constexpr int CG = D / 4;       // float4 column groups per row
-    constexpr int RG = 256 / CG;    // row groups (threads sharing a column group)
-    constexpr int RPT = D / RG;     // rows per thread
-    __shared__ float s_q[D], s_k[D], s_a[D], s_u[D];
-    __shared__ float s_red[2][RG][D];
+template <int D, int NT, int W, typename TI, typename TB, typename TO>
+__global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
+                                                    const TI *__restrict__ v, const float *__restrict__ g,
+                                                    const TB *__restrict__ beta, float *__restrict__ S,
+                                                    TO *__restrict__ out) {
+    // NT threads cover W columns of one chain: the reductions over key rows stay
+    // inside the workgroup, so the columns of a chain are split over D / W
+    // workgroups.
+    constexpr int CG = W / 4;         // float4 column groups per workgroup
+    constexpr int RG = NT / CG;       // row groups (threads sharing a column group)
+    constexpr int RPT = D / RG;       // rows per thread
+    static_assert(CG * RG == NT && RG * RPT == D, "decode tiling");
+    __shared__ float s_q[D], s_k[D], s_a[D], s_u[W];
+    __shared__ float s_red[2][RG][W];
     __shared__ float s_qk;
 
-    const size_t chain = blockIdx.x;
+    constexpr int SPLIT = D / W;
+    const size_t chain = blockIdx.x / SPLIT;
+    const int col0 = (blockIdx.x % SPLIT) * W;
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
-    f32x4 *Sp = reinterpret_cast<f32x4 *>(S + chain * D * D);
+    f32x4 *Sp = reinterpret_cast<f32x4 *>(S + chain * D * D + col0);
 
     f32x4 m[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) m[i] = __builtin_nontemporal_load(&Sp[(rg + RG * i) * CG + cg]);
+    for (int i = 0; i < RPT; ++i) m[i] = Sp[(rg + RG * i) * (D / 4) + cg];
 
-    if (t < D) {
-        s_q[t] = io<TI>::load(q, chain * D + t);
-        s_k[t] = io<TI>::load(k, chain * D + t);
-        s_a[t] = expf(g[chain * D + t]);
+    for (int c = t; c < D; c += NT) {
+        s_q[c] = io<TI>::load(q, chain * D + c);
+        s_k[c] = io<TI>::load(k, chain * D + c);
+        s_a[c] = expf(g[chain * D + c]);
     }
     __syncthreads();
     if (t < 64) {
@@ -63,14 +72,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const TI *__restrict__ q, c
     *reinterpret_cast<float4 *>(&s_red[0][rg][4 * cg]) = pk;
     *reinterpret_cast<float4 *>(&s_red[1][rg][4 * cg]) = pq;
     __syncthreads();
-    if (t < D) {
+    if (t < W) {
         float p = 0.f, r = 0.f;
 #pragma unroll
         for (int j = 0; j < RG; ++j) { p += s_red[0][j][t]; r += s_red[1][j][t]; }
         const float b = io<TB>::load(beta, chain);
-        const float u = b * (io<TI>::load(v, chain * D + t) - p);
+        const float u = b * (io<TI>::load(v, chain * D + col0 + t) - p);
         s_u[t] = u;
-        io<TO>::store(out, chain * D + t, r + s_qk * u);
+        io<TO>::store(out, chain * D + col0 + t, r + s_qk * u);
     }
     __syncthreads();
     const float4 u4 = *reinterpret_cast<const float4 *>(&s_u[4 * cg]);
@@ -80,14 +89,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const TI *__restrict__ q, c
         const float kr = s_k[r];
         f32x4 x = m[i];
         x.x += kr * u4.x; x.y += kr * u4.y; x.z += kr * u4.z; x.w += kr * u4.w;
-        __builtin_nontemporal_store(x, &Sp[r * CG + cg]);
+        __builtin_nontemporal_store(x, &Sp[r * (D / 4) + cg]);
     }
 }
 
+#ifndef KDA_DECODE_NT
+#define KDA_DECODE_NT 128
+#endif
+#ifndef KDA_DECODE_WDIV
+#define KDA_DECODE_WDIV 2
+#endif
+
 template <int D, typename TI, typename TB, typename TO>
 hipError_t launch_t(const DecodeArgs &a) {
+    constexpr int NT = KDA_DECODE_NT, W = D / KDA_DECODE_WDIV;
     const unsigned chains = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
-    hipLaunchKernelGGL((decode_kernel<D, TI, TB, TO>), dim3(chains), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((decode_kernel<D, NT, W, TI, TB, TO>), dim3(chains * (D / W)), dim3(NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
                        a.g, static_cast<const TB *>(a.beta), a.S, static_cast<TO *>(a.out));
     return hipGetLastError();
