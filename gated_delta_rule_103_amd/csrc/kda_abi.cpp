@@ -48,10 +48,15 @@ size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int
     return workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);
 }
 
-int kda_prefill(const void *q, const void *k, const void *v, const float *g, const void *beta,
-                const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B,
-                int T, int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
-                kda_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                 const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B, int T,
+                 int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
+                 int snapshot_every, int max_snapshots, float *snapshots, void *workspace,
+                 size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
     if (N < 1 || B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || C < 1) return KDA_ERR_INVALID_ARG;
     if (!dtype_ok(io_dtype) || !dtype_ok(beta_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_INVALID_ARG;
@@ -62,8 +67,13 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g, con
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
          reinterpret_cast<uintptr_t>(g)) & 15u)
         return KDA_ERR_INVALID_ARG;
+    if (snapshots) {
+        if (snapshot_every < 1 || max_snapshots < 1) return KDA_ERR_INVALID_ARG;
+        if ((long long)N * H * max_snapshots > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
+    }
     if (!head_dims_supported(Dk, Dv) || !chunk_supported(C)) return KDA_ERR_UNSUPPORTED;
     if (io_dtype == KDA_F32 && (beta_dtype != KDA_F32 || out_dtype != KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    if (snapshots && snapshot_every % C != 0) return KDA_ERR_UNSUPPORTED;
     const size_t need = workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KDA_ERR_WORKSPACE;
@@ -75,8 +85,36 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g, con
     a.out_dt = static_cast<Dt>(out_dtype);
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
+    if (snapshots) {
+        a.snaps = snapshots;
+        a.snap_every = snapshot_every / C;
+        a.max_snaps = max_snapshots;
+    }
     const hipError_t e = use_mfma(io_dtype) ? kda::launch_prefill_mfma(a) : kda::launch_prefill_f32(a);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_prefill(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B,
+                int T, int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
+                kda_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(q, k, v, g, beta, S0, out, S_out, cu_seqlens, N, B, T, H, Dk, Dv, C, io_dtype,
+                        beta_dtype, out_dtype, 0, 0, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kda_prefill_snapshots(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                          const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B,
+                          int T, int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
+                          kda_dtype out_dtype, int snapshot_every, int max_snapshots, float *snapshots,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (!snapshots) return KDA_ERR_INVALID_ARG;
+    return prefill_impl(q, k, v, g, beta, S0, out, S_out, cu_seqlens, N, B, T, H, Dk, Dv, C, io_dtype,
+                        beta_dtype, out_dtype, snapshot_every, max_snapshots, snapshots, workspace,
+                        workspace_bytes, stream);
 }
 
 int kda_decode(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,

@@ -33,4 +33,20 @@ struct SeqView {
     }
 };
 
+// Optional state snapshots for prefix caching: the state of a chain after the
+// first k * every chunks of its sequence (k = 1, 2, ..., up to max) goes to
+// base[((n * H + h) * max + k - 1) * Dk * Dv + ...]. Only boundaries inside the
+// sequence (k * every * C <= length) are written.
+struct SnapView {
+    float *base;    // [N][H][max][Dk][Dv] fp32, or nullptr
+    int every;      // chunks between snapshots (> 0 when base is set)
+    int max;        // snapshots per sequence
+    __device__ float *slot(int n, int h, int H, int chunks_done, int len, int C, int DD) const {
+        if (!base || chunks_done % every != 0 || chunks_done * C > len) return nullptr;
+        const int k = chunks_done / every;
+        if (k > max) return nullptr;
+        return base + (((size_t)n * H + h) * max + (k - 1)) * DD;
+    }
+};
+
 }  // namespace kda

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, con
 template <int C, int D, int TV, typename TO>
 __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ rec_base, const float *__restrict__ S0,
                                                    TO *__restrict__ out, float *__restrict__ S_out, SeqView sv,
-                                                   int H) {
+                                                   int H, SnapView snap) {
     using R = Rec<C, D>;
     __shared__ float s_M[D][TV];
     __shared__ float s_U[C][TV];
@@ -191,6 +191,12 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ rec
             s_M[c][jj] = m;
         }
         __syncthreads();
+        if (float *sp = snap.slot(n, h, H, j + 1, len, C, D * D)) {     // uniform across the workgroup
+            for (int p = t; p < D * TV; p += 256) {
+                const int c = p / TV, jj = p % TV;
+                sp[(size_t)c * D + j0 + jj] = s_M[c][jj];
+            }
+        }
     }
     if (S_out) {
         for (int p = t; p < D * TV; p += 256) {
@@ -222,7 +228,7 @@ hipError_t run(const PrefillArgs &a) {
     }
     (void)sizeof(R);
     hipLaunchKernelGGL((scan_kernel<C, D, TV, TO>), dim3(a.N, a.H, D / TV), dim3(256), 0, a.stream, recs, a.S0,
-                       static_cast<TO *>(a.out), a.S_out, sv, a.H);
+                       static_cast<TO *>(a.out), a.S_out, sv, a.H, SnapView{a.snaps, a.snap_every, a.max_snaps});
     return hipGetLastError();
 }
 

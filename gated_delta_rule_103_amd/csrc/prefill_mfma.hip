@@ -576,6 +576,7 @@ struct ScanParams {
     int H, chains;
     const char *rec;
     long long rec_stride;        // records per head
+    SnapView snap;
 };
 
 template <int TV, typename TO>
@@ -770,6 +771,17 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                 if (t < Lc) st_scalar<TO>(static_cast<TO *>(p.out), ((size_t)(tok0 + t) * H + h) * D + col, o);
             }
         }
+        if (float *sp = p.snap.slot(n, h, H, j + 1, end - start, C, D * D)) {   // uniform across the workgroup
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int chn = 32 * wave + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                        sp[(size_t)chn * D + col] = Macc[rt][nt][i];
+                    }
+        }
         publish_state();
         __syncthreads();
     };
@@ -868,7 +880,8 @@ hipError_t run(const PrefillArgs &a) {
         auto kern = chunk_scan_kernel<kTV, TO>;
         const int chains = a.N * a.H;
         const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * TEAM;
-        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc};
+        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc,
+                      SnapView{a.snaps, a.snap_every, a.max_snaps}};
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(NTHR), ScanLds<kTV>::SIZE, a.stream, sp);
         return hipGetLastError();
     }

@@ -50,6 +50,9 @@ def load_library() -> ctypes.CDLL:
     lib.kda_prefill.restype = i
     lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 i, i, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.kda_prefill_snapshots.restype = i
+    lib.kda_prefill_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          i, i, i, i, i, i, i, i, i, i, i, i, vp, vp, sz, vp]
     lib.kda_decode.restype = i
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     _lib = lib
@@ -82,6 +85,21 @@ def kda_prefill_workspace_size(N: int, T_total: int, H: int, Dk: int, Dv: int, C
     return int(load_library().kda_prefill_workspace_size(N, T_total, H, Dk, Dv, C, _DT[io_dtype]))
 
 
+def _prefill_buffers(lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state):
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty(B, T, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
+    if S_out is None and return_state:
+        S_out = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
+    need = int(lib.kda_prefill_workspace_size(N, B * T, H, Dk, Dv, C, _dt(q)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes
+
+
 def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
                 out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
                 return_state: bool = True):
@@ -89,24 +107,36 @@ def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=N
     S0: [N, H, Dk, Dv] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B == 1) or None.
     Returns (out [B, T, H, Dv], S_out [N, H, Dk, Dv] or None)."""
     lib = load_library()
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    od = out_dtype or q.dtype
-    if out is None:
-        out = torch.empty(B, T, H, Dv, dtype=od, device=q.device)
-    if S_out is None and return_state:
-        S_out = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
-    need = int(lib.kda_prefill_workspace_size(N, B * T, H, Dk, Dv, C, _dt(q)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
+        lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
     st = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
                          _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
                          _dt(out), _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise KDAError(st, "kda_prefill")
     return out, S_out
+
+
+def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max_snapshots: int,
+                          snapshots=None, out=None, S_out=None, cu_seqlens=None, C: int = 64,
+                          out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
+                          return_state: bool = True):
+    """kda_prefill that also writes the state after every ``snapshot_every`` tokens of
+    each sequence into ``snapshots`` [N, H, max_snapshots, Dk, Dv] fp32 (slots past a
+    sequence's end are not written). Returns (out, S_out, snapshots)."""
+    lib = load_library()
+    (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
+        lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
+    if snapshots is None:
+        snapshots = torch.full((N, H, max_snapshots, Dk, Dv), float("nan"), dtype=torch.float32,
+                               device=q.device)
+    st = lib.kda_prefill_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
+                                   _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q),
+                                   _dt(beta), _dt(out), snapshot_every, max_snapshots, _ptr(snapshots),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_snapshots")
+    return out, S_out, snapshots
 
 
 def kda_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,

@@ -116,6 +116,32 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_prefill_snapshots -- kda_prefill that also saves intermediate states
+ * for prefix caching. Linear attention keeps one fixed-size state per chain
+ * instead of a growing KV cache, so a prefix cache must hold the state at
+ * chosen token offsets (Explainer, KV-cache section: coarse fixed intervals
+ * plus prompt boundaries, the latter being S_out).
+ *
+ * All arguments as for kda_prefill, plus:
+ *   snapshot_every  tokens between snapshots, a multiple of C (else
+ *                   KDA_ERR_UNSUPPORTED), >= 1
+ *   max_snapshots   capacity per sequence, >= 1
+ *   snapshots       [N][H][max_snapshots][Dk][Dv] fp32 device buffer (not NULL).
+ *                   Slot k-1 of sequence n receives the state after its first
+ *                   k * snapshot_every tokens, for every k >= 1 with
+ *                   k * snapshot_every <= length(n) and k <= max_snapshots.
+ *                   Other slots are not written.
+ * Snapshots are exact intermediate states of the same computation (the values
+ * S_out would have for the truncated sequence, up to rounding).
+ */
+int kda_prefill_snapshots(const void *q, const void *k, const void *v, const float *g,
+                          const void *beta, const float *S0, void *out, float *S_out,
+                          const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                          int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
+                          int snapshot_every, int max_snapshots, float *snapshots,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_decode -- one token per sequence, state updated in place. This is one
  * step of the recurrence above (the explainer's decode paragraph: about
  * 7*D^2 FLOPs and about 8*D^2 bytes per head, the fp32 state being read and

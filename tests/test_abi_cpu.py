@@ -68,6 +68,26 @@ def test_prefill_argument_errors(lib, kw, status):
     assert _prefill(lib, **kw) == status
 
 
+def _prefill_snap(lib, every=64, max_snaps=2, snaps=ctypes.c_void_p(1 << 20), **kw):
+    fake = ctypes.c_void_p(256)
+    a = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, S0=None, out=fake, S_out=None,
+             cu=None, N=1, B=1, T=64, H=2, Dk=64, Dv=64, C=16, io=1, bd=1, od=1,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_snapshots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["out"],
+                                     a["S_out"], a["cu"], a["N"], a["B"], a["T"], a["H"], a["Dk"],
+                                     a["Dv"], a["C"], a["io"], a["bd"], a["od"], every, max_snaps,
+                                     snaps, a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("every,max_snaps,snaps,status", [
+    (64, 2, None, -1), (0, 2, ctypes.c_void_p(1 << 20), -1), (64, 0, ctypes.c_void_p(1 << 20), -1),
+    (24, 2, ctypes.c_void_p(1 << 20), -2),
+])
+def test_prefill_snapshots_argument_errors(lib, every, max_snaps, snaps, status):
+    assert _prefill_snap(lib, every, max_snaps, snaps) == status
+
+
 def test_prefill_workspace_misaligned(lib):
     need = lib.kda_prefill_workspace_size(1, 64, 2, 64, 64, 16, 1)
     assert need > 0
