@@ -50,24 +50,26 @@ def _time_region(fn, steps, warmup):
     return wall, per
 
 
-def bench_prefill(steps, warmup):
-    w = inputs.WORKLOADS[PREFILL_WORKLOAD]
-    p = inputs.workload_prefill(PREFILL_WORKLOAD, device="cuda")
-    B, T, H, D, C = w["B"], w["T"], w["H"], w["D"], w["C"]
+def bench_prefill(steps, warmup, workload=PREFILL_WORKLOAD):
+    w = inputs.WORKLOADS[workload]
+    p = inputs.workload_prefill(workload, device="cuda")
+    B, T, H, D, C = p.q.shape[0], p.q.shape[1], w["H"], w["D"], w["C"]
+    N = p.num_seqs
     out = torch.empty(B, T, H, D, dtype=torch.bfloat16, device="cuda")
-    S_out = torch.empty(B, H, D, D, dtype=torch.float32, device="cuda")
-    ws_n = kda_prefill_workspace_size(B, B * T, H, D, D, C, torch.bfloat16)
+    S_out = torch.empty(N, H, D, D, dtype=torch.float32, device="cuda")
+    ws_n = kda_prefill_workspace_size(N, B * T, H, D, D, C, torch.bfloat16)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
     def step():
-        kda_prefill(p.q, p.k, p.v, p.g, p.beta, None, out=out, S_out=S_out, C=C, workspace=ws)
+        kda_prefill(p.q, p.k, p.v, p.g, p.beta, p.S0, out=out, S_out=S_out, cu_seqlens=p.cu_seqlens,
+                    C=C, workspace=ws)
 
     wall, per = _time_region(step, steps, warmup)
     tokens = B * T
     ms = sum(per) / len(per)
     flops = costs.prefill_flops(tokens, H, C, D)
-    min_bytes = costs.prefill_min_bytes(tokens, H, D, D, B, io_bytes=2, beta_bytes=2)
-    return dict(tokens=tokens, wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=ms,
+    min_bytes = costs.prefill_min_bytes(tokens, H, D, D, N, io_bytes=2, beta_bytes=2, has_s0=p.S0 is not None)
+    return dict(tokens=tokens, seqs=N, wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=ms,
                 per_launch_ms=per, flops=flops, min_bytes=min_bytes, inputs=p)
 
 
@@ -142,6 +144,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default=PREFILL_WORKLOAD, choices=["single_seq_8k", "varlen_16x", "long_1m"],
+                    help="prefill workload to time (the metric is quoted on single_seq_8k)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the bench, run a plain device copy of MIB MiB three times "
                          "(the known-size reference that scales HBM counter readings)")
@@ -152,7 +156,7 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    pf = bench_prefill(args.steps, args.warmup)
+    pf = bench_prefill(args.steps, args.warmup, args.workload)
     peak_tf = costs.MI355X_PEAK["bf16_TFLOPs"]
     peak_bw = costs.MI355X_PEAK["hbm_GBps"]
     k_s = pf["kernel_ms"] * 1e-3
@@ -160,9 +164,9 @@ def main():
     gbps = pf["min_bytes"] / k_s / 1e9
     value = pf["tokens"] * args.steps / pf["wall_s"] / 1e6
     dec = None if args.no_decode else bench_decode(max(1, args.steps // 4), 1)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(pf["inputs"])
+    cpu = None if (args.no_cpu_baseline or args.workload != PREFILL_WORKLOAD) else cpu_baseline(pf["inputs"])
 
-    w = inputs.WORKLOADS[PREFILL_WORKLOAD]
+    w = inputs.WORKLOADS[args.workload]
     line = {
         "metric": "KDA prefill Mtokens/s (H=32,D=128,C=64) + decode achieved HBM GB/s vs peak",
         "value": round(value, 3),
@@ -176,12 +180,13 @@ def main():
         "vs_baseline": None,
         "dtype": PREFILL_DTYPE,
         "data": "synthetic",
-        "config": {"workload": PREFILL_WORKLOAD, "B": w["B"], "T": w["T"], "H": w["H"],
-                   "Dk": w["D"], "Dv": w["D"], "C": w["C"], "io": "bf16 q/k/v/o/beta, fp32 g/state",
-                   "gate": "-softplus(N(0,1)+2)"},
+        "config": {"workload": args.workload, "sequences": pf["seqs"], "tokens": pf["tokens"],
+                   "H": w["H"], "Dk": w["D"], "Dv": w["D"], "C": w["C"],
+                   "io": "bf16 q/k/v/o/beta, fp32 g/state",
+                   "gate": f"-softplus(N(0,1)+{w['shift']:g})"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf,
                      "unit": "TFLOP/s", "frac": round(tflops / peak_tf, 4),
-                     "traffic": measured_traffic("kda_prefill", PREFILL_WORKLOAD),
+                     "traffic": measured_traffic("kda_prefill", args.workload),
                      "kernel": "kda_prefill call (chunk_prep_kernel + chunk_scan_kernel)",
                      "model": "12C^3+8C^2D+6CD^2 FLOP per chunk-head",
                      "kernel_ms": round(pf["kernel_ms"], 4)},
