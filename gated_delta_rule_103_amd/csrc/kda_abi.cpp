@@ -72,6 +72,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
         if ((long long)N * H * max_snapshots > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
     }
     if (!head_dims_supported(Dk, Dv) || !chunk_supported(C)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)H * Dv * C * 4 > INT_MAX) return KDA_ERR_UNSUPPORTED;
     if (io_dtype == KDA_F32 && (beta_dtype != KDA_F32 || out_dtype != KDA_F32)) return KDA_ERR_UNSUPPORTED;
     if (snapshots && snapshot_every % C != 0) return KDA_ERR_UNSUPPORTED;
     const size_t need = workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);

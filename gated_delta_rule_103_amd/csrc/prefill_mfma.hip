@@ -78,6 +78,25 @@ __device__ __forceinline__ bf16x8 lds8(const __bf16 *p) { return *reinterpret_ca
 __device__ __forceinline__ f16x8 lds8h(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 __device__ __forceinline__ float bf2f(__bf16 x) { return static_cast<float>(x); }
 
+// Raw buffer access: a wave-uniform base and byte range held in scalar
+// registers, plus a 32-bit per-lane offset. A load past the range reads 0 and
+// a store past it is dropped, so the ragged tail of a sequence needs no
+// branch, and no per-lane 64-bit address arithmetic is spent per access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+template <typename T> __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, int voff, float x);
+template <> __device__ __forceinline__ void buf_st<float>(__amdgpu_buffer_rsrc_t r, int voff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, 0, 0);
+}
+template <> __device__ __forceinline__ void buf_st<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)), r, voff, 0, 0);
+}
+
 template <typename T> __device__ __forceinline__ float ld_scalar(const T *p, size_t i);
 template <> __device__ __forceinline__ float ld_scalar<float>(const float *p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld_scalar<bf16_t>(const bf16_t *p, size_t i) {
@@ -639,50 +658,76 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
     struct Frags {
         f16x8 kd[4], qd[4], ib[2], mq[2], kr[2][2];
         f32x4 dg, gam[2];
-        uint32_t v[NT][4];        // the 32-bit word holding the bf16 value; unpacked where used,
-                                  // so no instruction right after the load waits for it
+        uint32_t v[NT][4];        // bf16 bits of V (tokens tb + 4lq + i, column l16 of tile nt)
     };
-    auto load = [&](int j, Frags &f) {
-        const char *rec = p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES;
-        const char *rw = rec + (size_t)wave * Rec::WAVE + lane * 16;
+    // loop-invariant byte offsets of this lane's record fragments, and of its
+    // (token tb + 4lq + i, column col0 + 16nt + l16) elements from a chunk's
+    // first row in v (bf16) and in out
+    const int r_frag = wave * Rec::WAVE + lane * 16;
+    const int r_dg = (tb + 4 * lq) * 4, r_gam = (32 * wave + 4 * lq) * 4;
+    int v_off[NT][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            f.kd[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::KD + ks * 1024);
-            f.qd[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::QD + ks * 1024);
-        }
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            f.ib[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::IB + ks * 1024);
-            f.mq[ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::MQ + ks * 1024);
-        }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                f.kr[rt][ks] = *reinterpret_cast<const f16x8 *>(rw + Rec::KR + (rt * 2 + ks) * 1024);
-        // d for rows tb + 4lq .. +3 and gamma for channels 32w + 16rt + 4lq .. +3: one
-        // 16-byte load each (few load instructions keep two chunks within vmcnt's range)
-        f.dg = *reinterpret_cast<const f32x4 *>(rec + Rec::DG + (tb + 4 * lq) * 4);
-        f.gam[0] = *reinterpret_cast<const f32x4 *>(rec + Rec::GAM + (32 * wave + 4 * lq) * 4);
-        f.gam[1] = *reinterpret_cast<const f32x4 *>(rec + Rec::GAM + (32 * wave + 16 + 4 * lq) * 4);
-        // rows past the end of the sequence read the last row: their values never
-        // matter, because beta = 0 there makes the matching rows and columns of IB
-        // zero. No select right after the load, so nothing waits on loads in flight.
+        for (int i = 0; i < 4; ++i) v_off[nt][i] = ((tb + 4 * lq + i) * H * D + col0 + 16 * nt + l16) * 2;
+    // bytes from a chunk's first row to the end of its last valid row
+    auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
+
+    // The loads of one chunk's operands, as NLD slots in the order they are
+    // consumed: Kd and Qd by k-step, V, IB, gamma, Kr, Mqk, d. issue() sends
+    // slots [s0, s1); the step spreads them over its phases, so that no wave
+    // stalls on a full vector-memory queue with work of its own waiting.
+    constexpr int NLD = 19 + 4 * NT;
+    auto issue = [&](int j, Frags &f, int s0, int s1) {
+        const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
         const int tok0 = start + j * C, Lc = min(C, end - tok0);
+        // rows past the end of the sequence read 0 (outside the range): their values
+        // never matter, because beta = 0 there makes the matching columns of IB zero
+        const auto rv = buf_rsrc(p.v + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, 2));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tc = min(tb + 4 * lq + i, Lc - 1);
-                const size_t e = ((size_t)(tok0 + tc) * H + h) * D + col0 + 16 * nt + l16;
-                f.v[nt][i] = reinterpret_cast<const uint32_t *>(p.v)[e >> 1];
+        for (int sl = 0; sl < NLD; ++sl) {
+            if (sl < s0 || sl >= s1) continue;
+            if (sl < 8) {
+                const int ks = sl >> 1;
+                if (sl & 1) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
+                else f.kd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + ks * 1024);
+            } else if (sl < 8 + 4 * NT) {
+                const int e = sl - 8;
+                f.v[e >> 2][e & 3] = __builtin_amdgcn_raw_buffer_load_b16(rv, v_off[e >> 2][e & 3], 0, 0);
+            } else {
+                const int e = sl - 8 - 4 * NT;
+                if (e < 2) f.ib[e] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + e * 1024);
+                // gamma for channels 32w + 16rt + 4lq .. +3 and d for rows tb + 4lq .. +3
+                else if (e < 4) f.gam[e - 2] = buf_ld16<f32x4>(rr, r_gam, Rec::GAM + (e - 2) * 64);
+                else if (e < 8) f.kr[(e - 4) >> 1][(e - 4) & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + (e - 4) * 1024);
+                else if (e < 10) f.mq[e - 8] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + (e - 8) * 1024);
+                else f.dg = buf_ld16<f32x4>(rr, r_dg, Rec::DG);
             }
+            // keep the slot order: the in-order vmcnt then lets each use wait
+            // for its own load only
+            __builtin_amdgcn_sched_barrier(0x048F);
+        }
+    };
+    // where a step issues the next operands: Kd, Qd and V before its first
+    // product (START), IB and gamma after the first k-step of U (U0), Kr, Mqk
+    // and d after the first k-step of the state update (M0). Issued all at
+    // once, the 23 loads stall the wave on a full vector-memory queue.
+    enum { START, U0, M0 };
+    auto issue_at = [&](int nj, Frags &nf, int point) {
+        constexpr int NV = 8 + 4 * NT;        // Kd, Qd and V
+        const int a = point == START ? 0 : point == U0 ? NV : NV + 4;
+        const int b = point == START ? NV : point == U0 ? NV + 4 : NLD;
+        issue(nj, nf, a, b);
+        // the loads stay where they are issued; compute and LDS traffic may cross
+        __builtin_amdgcn_sched_barrier(0x048F);
     };
 
     // Three operand buffers, used round-robin without copies: the loads for a chunk
     // are issued two chunks before it is consumed.
-    auto step = [&](const Frags &f, int j) {
+    auto step = [&](const Frags &f, int j, Frags &nf, int nj) {
         const int tok0 = start + j * C, Lc = min(C, end - tok0);
+        const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, sizeof(TO)));
+        issue_at(nj, nf, START);
 
         // X = Kd M and O = Qd M for tokens tb..tb+15 (state split hi + lo)
         f32x4 accX[NT], accO[NT], Ureg[NT];
@@ -706,9 +751,7 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
             f16x4 hi, lo;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // element parity = l16 parity (row offsets and col0 are even)
-                const uint32_t w = f.v[nt][i];
-                const float vv = __uint_as_float((l16 & 1) ? (w & 0xffff0000u) : (w << 16));
+                const float vv = __uint_as_float(f.v[nt][i] << 16);
                 SPLITH(vv - accX[nt][i], hi[i], lo[i]);
             }
             const int col = 16 * nt + l16, t = tb + 4 * lq;
@@ -728,6 +771,7 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
 #if KDA_SPLIT_Y
                 u = mfma_f16(f.ib[ks], bl, u);
 #endif
+                if (nt == 0 && ks == 0) issue_at(nj, nf, U0);
             }
             Ureg[nt] = u;
             f16x4 hi, lo;
@@ -761,15 +805,12 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
 #if KDA_SPLIT_UO
                 accO[nt] = mfma_f16(f.mq[ks], bl, accO[nt]);
 #endif
+                if (nt == 0 && ks == 0) issue_at(nj, nf, M0);
             }
-            // + diag(q.k) U with U in fp32, then store
-            const int col = col0 + 16 * nt + l16;
+            // + diag(q.k) U with U in fp32, then store (rows past the end are dropped)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tb + 4 * lq + i;
-                const float o = accO[nt][i] + f.dg[i] * Ureg[nt][i];
-                if (t < Lc) st_scalar<TO>(static_cast<TO *>(p.out), ((size_t)(tok0 + t) * H + h) * D + col, o);
-            }
+            for (int i = 0; i < 4; ++i)
+                buf_st<TO>(ro, v_off[nt][i] * (int)(sizeof(TO) / 2), accO[nt][i] + f.dg[i] * Ureg[nt][i]);
         }
         if (float *sp = p.snap.slot(n, h, H, j + 1, end - start, C, D * D)) {   // uniform across the workgroup
 #pragma unroll
@@ -791,17 +832,14 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
     Frags A, B, Cb;
     if (nch > 0) {
         const int last = nch - 1;
-        load(0, A);
-        load(min(1, last), B);
+        issue(0, A, 0, NLD);
+        issue(min(1, last), B, 0, NLD);
         for (int j = 0; j < nch; j += 3) {
-            load(min(j + 2, last), Cb);
-            step(A, j);
+            step(A, j, Cb, min(j + 2, last));
             if (j + 1 >= nch) break;
-            load(min(j + 3, last), A);
-            step(B, j + 1);
+            step(B, j + 1, A, min(j + 3, last));
             if (j + 2 >= nch) break;
-            load(min(j + 4, last), B);
-            step(Cb, j + 2);
+            step(Cb, j + 2, B, min(j + 4, last));
         }
     }
 

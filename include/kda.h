@@ -96,7 +96,8 @@ size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int
  * not depend on C beyond rounding.
  *
  * Support matrix (else KDA_ERR_UNSUPPORTED):
- *   Dk == Dv in {64, 128}; C in {16, 32, 64};
+ *   Dk == Dv in {64, 128}; C in {16, 32, 64}; H * Dv * C * 4 <= INT_MAX (the
+ *     kernels address one chunk of a token-major tensor with 32-bit offsets);
  *   io_dtype KDA_F32: fp32 arithmetic throughout, beta_dtype and out_dtype
  *     must be KDA_F32;
  *   io_dtype KDA_BF16: bf16 q/k/v with bf16 MFMA contractions and fp32

@@ -59,6 +59,7 @@ def _prefill(lib, **kw):
     (dict(cu=ctypes.c_void_p(512), B=2, N=2), -1),
     (dict(Dk=96, Dv=96), -2), (dict(Dk=64, Dv=128), -2), (dict(C=8), -2), (dict(C=128), -2),
     (dict(io=0, bd=1, od=0), -2), (dict(io=0, bd=0, od=1), -2),
+    (dict(H=70000, Dk=128, Dv=128, C=64), -2),     # a chunk spans more than 2^31 bytes
     (dict(ws=None, wsb=0, io=0, bd=0, od=0), -3),
     (dict(q=ctypes.c_void_p(264)), -1), (dict(g=ctypes.c_void_p(260)), -1),
     (dict(v=ctypes.c_void_p(258)), -1),
