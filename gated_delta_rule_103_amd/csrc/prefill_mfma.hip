@@ -228,35 +228,48 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     f32x4 rg[4];
     TB rbeta = TB(0);
     int nx_h = 0, nx_tok0 = 0, nx_Lc = 0;
-    auto fetch = [&](int item) {
-        const int ci = item / H, h = item % H;
-        int2 m;
-        if constexpr (VARLEN) {
-            m = meta_ahead;
-            meta_ahead = p.meta[min(item + (int)gridDim.x, items - 1) / H];
-        } else {
-            m = dense_meta(ci);
+    // part 0: chunk bounds, q and k; part 1: g; part 2: beta; -1: all. The
+    // parts go out in different phases of the current item, so that no phase
+    // stalls on a full vector-memory queue.
+    auto fetch = [&](int item, int part) {
+        if (part <= 0) {
+            const int ci = item / H;
+            int2 m;
+            if constexpr (VARLEN) {
+                m = meta_ahead;
+                meta_ahead = p.meta[min(item + (int)gridDim.x, items - 1) / H];
+            } else {
+                m = dense_meta(ci);
+            }
+            nx_h = item % H;
+            nx_tok0 = m.x;
+            nx_Lc = m.y;
         }
-        const int tok0 = m.x, Lc = m.y;
-        nx_h = h;
-        nx_tok0 = tok0;
-        nx_Lc = Lc;
+        const int h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
+        if (part <= 0) {
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int idx = tid0 + it * PTHR, row = idx >> 4, part = idx & 15;
-            const size_t off = ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 8 * part;
-            rq[it] = *reinterpret_cast<const u32x4 *>(p.q + off);
-            rk[it] = *reinterpret_cast<const u32x4 *>(p.k + off);
+            for (int it = 0; it < 2; ++it) {
+                const int idx = tid0 + it * PTHR, row = idx >> 4, part = idx & 15;
+                const size_t off = ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 8 * part;
+                rq[it] = *reinterpret_cast<const u32x4 *>(p.q + off);
+                rk[it] = *reinterpret_cast<const u32x4 *>(p.k + off);
+            }
         }
+        if (part == -1 || part == 1) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid0 + it * PTHR, row = idx >> 5, part = idx & 31;
-            rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
+            for (int it = 0; it < 4; ++it) {
+                const int idx = tid0 + it * PTHR, row = idx >> 5, part = idx & 31;
+                rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
+            }
         }
-        rbeta = static_cast<const TB *>(p.beta)[(size_t)(tok0 + min(tid0 & 63, Lc - 1)) * H + h];
+        if (part == -1 || part == 2)
+            rbeta = static_cast<const TB *>(p.beta)[(size_t)(tok0 + min(tid0 & 63, Lc - 1)) * H + h];
     };
-    if ((int)blockIdx.x < items) fetch(blockIdx.x);
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    // One item: stage, decays, L / Mqk, inverse, record. The first item is a
+    // separate copy of the body, so that the loop is entered only from the end of
+    // an item: the compiler's wait for the next item's inputs then counts the
+    // record stores issued after them and does not wait for those stores.
+    auto body = [&](int item) __attribute__((always_inline)) {
         const int ci = item / H, h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
         // per-thread LDS addresses are recomputed every item instead of being
         // hoisted out of the loop and held in registers for its whole length
@@ -282,8 +295,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         }
         if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
         if (tid < 4) sFlag[tid] = 0;
-        fetch(min(item + (int)gridDim.x, items - 1));
         __syncthreads();
+        // the next item's inputs, in flight while this one is computed
+        const int next = min(item + (int)gridDim.x, items - 1);
+        fetch(next, 0);
 
         // ================= in-block suffix (F) and prefix (E) products of alpha
         {
@@ -327,6 +342,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             sMqk[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<_Float16>(0.f);
         }
         __syncthreads();
+        fetch(next, 1);
         if (tid < D) {
             const int c = tid;
             const float g0 = sGB[c], g1 = sGB[D + c], g2 = sGB[2 * D + c], g3 = sGB[3 * D + c];
@@ -455,6 +471,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         __syncthreads();
+        fetch(next, 2);
 
         // ================= INV = (I + L)^{-1}, stored transposed in the upper triangle
         // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II
@@ -511,13 +528,17 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         }
 
         // ================= record: fp16 fragments of the scan's left operands
-        // waves 0-3: tokens 16w..16w+15 (Kd, Qd, IB, Mqk); waves 4-7: channels
-        // 32(w-4)..+31 (Kr^T). Record role r = wave & 3.
+        // Record role r = wave & 3 (tokens 16r..16r+15, channels 32r..32r+31).
+        // Waves 0-3 build Kd and Qd; waves 4-7 build Kr^T, IB and Mqk. Both store
+        // eight fragments from the same code after the branch: stores inside
+        // role branches would leave the compiler a path without them, and its
+        // wait for the next item's inputs would then also wait for the stores.
         {
             const int role = wave & 3;
-            char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES + (size_t)role * Rec::WAVE;
+            const int t = 16 * role + l16;
+            f16x8 fr[8];
             if (wave < 4) {
-                const int t = 16 * role + l16, I = role;
+                const int I = role;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c0 = 32 * ks + 8 * lq;
@@ -526,52 +547,62 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
                     const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0);
                     const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0 + 4);
-                    f16x8 kd, qd;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
-                        kd[e] = static_cast<_Float16>(bf2f(kx[e]) * dec);
-                        qd[e] = static_cast<_Float16>(bf2f(qx[e]) * dec);
+                        fr[ks][e] = static_cast<_Float16>(bf2f(kx[e]) * dec);
+                        fr[4 + ks][e] = static_cast<_Float16>(bf2f(qx[e]) * dec);
                     }
-                    *reinterpret_cast<f16x8 *>(rec + Rec::KD + ks * 1024 + lane * 16) = kd;
-                    *reinterpret_cast<f16x8 *>(rec + Rec::QD + ks * 1024 + lane * 16) = qd;
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    f16x8 ib;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int sc = 32 * ks + 8 * lq + e;
-                        // INV[t][sc] is stored at (sc, t); zero for sc > t
-                        const float x = (sc <= t) ? sLI[sc * SL + t] * sBeta[sc] : 0.f;
-                        ib[e] = static_cast<_Float16>(x);
-                    }
-                    *reinterpret_cast<f16x8 *>(rec + Rec::IB + ks * 1024 + lane * 16) = ib;
-                    *reinterpret_cast<f16x8 *>(rec + Rec::MQ + ks * 1024 + lane * 16) =
-                        *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
                 }
             } else {
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     const int chn = 32 * role + 16 * rt + l16;
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        f16x8 kr;
+                    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int tt = 32 * ks + 8 * lq + e;
-                            kr[e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] * sH[(tt >> 4) * D + chn]);
+                            fr[rt * 2 + ks][e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] *
+                                                                       sH[(tt >> 4) * D + chn]);
                         }
-                        *reinterpret_cast<f16x8 *>(rec + Rec::KR + (rt * 2 + ks) * 1024 + lane * 16) = kr;
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int sc = 32 * ks + 8 * lq + e;
+                        // INV[t][sc] is stored at (sc, t); zero for sc > t. Both reads are
+                        // unconditional (in bounds), so no branch waits on each of them.
+                        const float x = sLI[sc * SL + t] * sBeta[sc];
+                        fr[4 + ks][e] = static_cast<_Float16>(sc <= t ? x : 0.f);
                     }
+                    fr[6 + ks] = *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
                 }
             }
-            char *tail = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES;
-            if (tid < C) reinterpret_cast<float *>(tail + Rec::DG)[tid] = sDg[tid];
-            if (tid < D) reinterpret_cast<float *>(tail + Rec::GAM)[tid] = sGam[tid];
+            // fragment i: waves 0-3 Kd (i < 4) and Qd, contiguous from KD; waves 4-7
+            // Kr (i < 4), then IB and Mqk, contiguous from IB
+            static_assert(Rec::QD == Rec::KD + 4096 && Rec::MQ == Rec::IB + 2048, "record layout");
+            char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES;
+            char *rw = rec + (size_t)role * Rec::WAVE + lane * 16;
+            const int o_lo = wave < 4 ? Rec::KD : Rec::KR, o_hi = wave < 4 ? Rec::KD : Rec::IB - 4096;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<f16x8 *>(rw + (i < 4 ? o_lo : o_hi) + i * 1024) = fr[i];
+            // d (64 floats) then gamma (128 floats): one float per thread, every
+            // thread issues the store and the range check drops those past the end
+            static_assert(Rec::GAM == Rec::DG + C * 4, "record layout");
+            const float tv = tid < C ? sDg[tid] : sGam[min(tid - C, D - 1) & (D - 1)];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tv),
+                                                  buf_rsrc(rec + Rec::DG, (C + D) * 4), tid * 4, 0, 0);
         }
         __syncthreads();      // LDS is restaged by the next item
+    };
+    if ((int)blockIdx.x < items) {
+        fetch(blockIdx.x, -1);
+        body(blockIdx.x);
     }
+    for (int item = blockIdx.x + gridDim.x; item < items; item += gridDim.x) body(item);
 }
 
 // ---------------------------------------------------------------- scan
