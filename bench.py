@@ -32,22 +32,23 @@ PREFILL_DTYPE = "bf16"
 
 
 def _time_region(fn, steps, warmup):
-    """Run warmup untimed, then time exactly `steps` calls with events on the
-    current stream (the one the library launches on), synchronised on both sides."""
+    """Run warmup untimed, then time exactly `steps` back-to-back calls,
+    synchronised on both sides: host wall clock for the region, and one pair
+    of events on the current stream (the one the library launches on)
+    bracketing the same calls, whose elapsed time / steps is the average device
+    duration of one call. Events between calls would add a gap to every call."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record()
+    a.record()
+    for _ in range(steps):
         fn()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in ev]          # ms per launch
-    return wall, per
+    return wall, a.elapsed_time(b) / steps        # s, ms per call
 
 
 def bench_prefill(steps, warmup, workload=PREFILL_WORKLOAD):
@@ -64,13 +65,12 @@ def bench_prefill(steps, warmup, workload=PREFILL_WORKLOAD):
         kda_prefill(p.q, p.k, p.v, p.g, p.beta, p.S0, out=out, S_out=S_out, cu_seqlens=p.cu_seqlens,
                     C=C, workspace=ws)
 
-    wall, per = _time_region(step, steps, warmup)
+    wall, ms = _time_region(step, steps, warmup)
     tokens = B * T
-    ms = sum(per) / len(per)
     flops = costs.prefill_flops(tokens, H, C, D)
     min_bytes = costs.prefill_min_bytes(tokens, H, D, D, N, io_bytes=2, beta_bytes=2, has_s0=p.S0 is not None)
     return dict(tokens=tokens, seqs=N, wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=ms,
-                per_launch_ms=per, flops=flops, min_bytes=min_bytes, inputs=p)
+                flops=flops, min_bytes=min_bytes, inputs=p)
 
 
 def bench_decode(steps, warmup):
@@ -84,8 +84,8 @@ def bench_decode(steps, warmup):
         for s in range(nsteps):
             kda_decode(x.q[s], x.k[s], x.v[s], x.g[s], x.beta[s], S, out=out)
 
-    wall, per = _time_region(one_pass, steps, warmup)
-    ms_step = (sum(per) / len(per)) / nsteps
+    wall, ms_pass = _time_region(one_pass, steps, warmup)
+    ms_step = ms_pass / nsteps
     N, H, D = w["N"], w["H"], w["D"]
     state_bytes = costs.decode_bytes_per_head(D) * N * H
     vec_bytes = costs.decode_vector_bytes(N, H, D, D)

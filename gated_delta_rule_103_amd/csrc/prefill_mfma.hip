@@ -355,39 +355,35 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // Left operands x_t E_t (x = k for L, q for Mqk), t in block I.
         // Diagonal blocks (wavefronts 0-3, I = J = wavefront): right operands k_s / E_s
         // (start of block as reference, bounded by 1 / Gamma_I; a block with Gamma_I
-        // below FLT_MIN takes the exact path instead), both operands split into bf16
-        // hi + lo (three products per k-step): near-diagonal entries dominate o.
-        // Off-diagonal blocks (wavefronts 4-6, two blocks each): right operands
-        // k_s F_s prod_{J<K<I} Gamma_K; every factor is <= 1, so both operands are
-        // rounded once to fp16 (11-bit significand) and multiplied on fp16 MFMA.
-        //   wavefront 4: (3,0) (3,1)   5: (3,2) (1,0)   6: (2,0) (2,1)
+        // below FLT_MIN takes the exact path instead), multiplied in fp32 on
+        // v_mfma_f32_16x16x4f32: near-diagonal entries dominate o, and fp32
+        // operands need no hi/lo splitting on the vector ALU.
+        // Off-diagonal blocks (wavefronts 4-7): right operands k_s F_s
+        // prod_{J<K<I} Gamma_K; every factor is <= 1, so both operands are rounded
+        // once to fp16 (11-bit significand) and multiplied on fp16 MFMA. A wave's
+        // blocks share their row block, so its left operands are built once.
+        //   wavefront 4: (3,0) (3,1)   5: (3,2)   6: (2,0) (2,1)   7: (1,0)
         if (wave < 4) {
             const int I = wave;
             if (!sFlag[I]) {
                 const int t = 16 * I + l16;
                 f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
-#pragma unroll 1
+#pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
+                    // lane: row / column t, channels 32ks + 8lq + e; product e contracts
+                    // channels 32ks + 8j + e over the four k-slots j
                     const int c0 = 32 * ks + 8 * lq;
                     const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
                     const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
                     const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-                    bf16x8 aqh, aql, akh, akl, bkh, bkl;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float ee = e < 4 ? e0[e] : e1[e - 4];
-                        SPLIT2(bf2f(qv[e]) * ee, aqh[e], aql[e]);
-                        SPLIT2(bf2f(kv[e]) * ee, akh[e], akl[e]);
-                        // same rows: the right operand is k_s / E_s
-                        SPLIT2(bf2f(kv[e]) * __builtin_amdgcn_rcpf(ee), bkh[e], bkl[e]);
+                        const float kk = bf2f(kv[e]);
+                        const float bk = kk * __builtin_amdgcn_rcpf(ee);
+                        accL = __builtin_amdgcn_mfma_f32_16x16x4f32(kk * ee, bk, accL, 0, 0, 0);
+                        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(bf2f(qv[e]) * ee, bk, accM, 0, 0, 0);
                     }
-                    // (lane l16 holds row t as left operand and column s = t as right operand)
-                    accL = mfma_bf16(akh, bkh, accL);
-                    accM = mfma_bf16(aqh, bkh, accM);
-                    accL = mfma_bf16(akh, bkl, accL);
-                    accM = mfma_bf16(aqh, bkl, accM);
-                    accL = mfma_bf16(akl, bkh, accL);
-                    accM = mfma_bf16(aql, bkh, accM);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -398,43 +394,53 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
                 }
             }
-        } else if (wave < 7) {
-            const int I0 = wave == 6 ? 2 : 3, J0 = wave == 5 ? 2 : 0;
-            const int I1 = wave == 4 ? 3 : (wave == 5 ? 1 : 2), J1 = wave == 5 ? 0 : 1;
+        } else {
+            const int I = wave == 6 ? 2 : wave == 7 ? 1 : 3;
+            const int nb = (wave == 5 || wave == 7) ? 1 : 2;
+            const int J0 = wave == 5 ? 2 : 0, J1 = 1;
             f32x4 accL[2], accM[2];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) { accL[bb] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[bb] = accL[bb]; }
-#pragma unroll 1
+            const int t = 16 * I + l16;
+#pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 32 * ks + 8 * lq;
+                const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
+                const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                f16x8 aq, ak;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float fa = e < 4 ? a0[e] : a1[e - 4];
+                    aq[e] = static_cast<_Float16>(bf2f(qv[e]) * fa);
+                    ak[e] = static_cast<_Float16>(bf2f(kv[e]) * fa);
+                }
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {
-                    const int I = bb ? I1 : I0, J = bb ? J1 : J0;
-                    const int t = 16 * I + l16, sr = 16 * J + l16;
-                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0), sv = lds8(sK + sr * SQ + c0);
-                    f32x4 a0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                    f32x4 a1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    if (bb >= nb) break;                     // uniform across the wavefront
+                    const int J = bb ? J1 : J0, sr = 16 * J + l16;
+                    const bf16x8 sv = lds8(sK + sr * SQ + c0);
                     f32x4 b0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
                     f32x4 b1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
-                    for (int K2 = J + 1; K2 < I; ++K2) {
-                        b0 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0);
-                        b1 *= *reinterpret_cast<const f32x4 *>(sGB + K2 * D + c0 + 4);
-                    }
-                    f16x8 aq, ak, bk;
+                    // prod_{J<K<I} Gamma_K, at most two factors (I - J <= 3); both rows
+                    // are read unconditionally (clamped) and unused factors are ones
+                    const float *gA = sGB + (J + 1) * D + c0, *gB = sGB + min(J + 2, 3) * D + c0;
+                    const f32x4 one = {1.f, 1.f, 1.f, 1.f};
+                    const f32x4 a0v = *reinterpret_cast<const f32x4 *>(gA), a1v = *reinterpret_cast<const f32x4 *>(gA + 4);
+                    const f32x4 c0v = *reinterpret_cast<const f32x4 *>(gB), c1v = *reinterpret_cast<const f32x4 *>(gB + 4);
+                    b0 *= (I - J >= 2 ? a0v : one) * (I - J == 3 ? c0v : one);
+                    b1 *= (I - J >= 2 ? a1v : one) * (I - J == 3 ? c1v : one);
+                    f16x8 bk;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float fa = e < 4 ? a0[e] : a1[e - 4], fb = e < 4 ? b0[e] : b1[e - 4];
-                        aq[e] = static_cast<_Float16>(bf2f(qv[e]) * fa);
-                        ak[e] = static_cast<_Float16>(bf2f(kv[e]) * fa);
-                        bk[e] = static_cast<_Float16>(bf2f(sv[e]) * fb);
-                    }
+                    for (int e = 0; e < 8; ++e) bk[e] = static_cast<_Float16>(bf2f(sv[e]) * (e < 4 ? b0[e] : b1[e - 4]));
                     accL[bb] = mfma_f16(ak, bk, accL[bb]);
                     accM[bb] = mfma_f16(aq, bk, accM[bb]);
                 }
             }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
-                const int I = bb ? I1 : I0, J = bb ? J1 : J0;
+                if (bb >= nb) break;
+                const int J = bb ? J1 : J0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = 16 * I + 4 * lq + i, sc = 16 * J + l16;
