@@ -565,22 +565,26 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 for (int rt = 0; rt < 2; ++rt) {
                     const int chn = 32 * role + 16 * rt + l16;
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
+                    for (int ks = 0; ks < 2; ++ks) {
+                        // tokens 32ks + 8lq .. +7 lie in one 16-token block
+                        const float hb = sH[(2 * ks + (lq >> 1)) * D + chn];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int tt = 32 * ks + 8 * lq + e;
-                            fr[rt * 2 + ks][e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] *
-                                                                       sH[(tt >> 4) * D + chn]);
+                            fr[rt * 2 + ks][e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] * hb);
                         }
+                    }
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
+                    const f32x4 be0 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq);
+                    const f32x4 be1 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq + 4);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int sc = 32 * ks + 8 * lq + e;
-                        // INV[t][sc] is stored at (sc, t); zero for sc > t. Both reads are
+                        // INV[t][sc] is stored at (sc, t); zero for sc > t. The read is
                         // unconditional (in bounds), so no branch waits on each of them.
-                        const float x = sLI[sc * SL + t] * sBeta[sc];
+                        const float x = sLI[sc * SL + t] * (e < 4 ? be0[e] : be1[e - 4]);
                         fr[4 + ks][e] = static_cast<_Float16>(sc <= t ? x : 0.f);
                     }
                     fr[6 + ks] = *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
