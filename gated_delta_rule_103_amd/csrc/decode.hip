@@ -24,7 +24,7 @@ template <int D, int NT, int W, typename TI, typename TB, typename TO>
 __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                     const TI *__restrict__ v, const float *__restrict__ g,
                                                     const TB *__restrict__ beta, float *__restrict__ S,
-                                                    TO *__restrict__ out) {
+                                                    TO *__restrict__ out, bool g_head) {
     // NT threads cover W columns of one chain: the reductions over key rows stay
     // inside the workgroup, so the columns of a chain are split over D / W
     // workgroups.
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, co
     for (int c = t; c < D; c += NT) {
         s_q[c] = io<TI>::load(q, chain * D + c);
         s_k[c] = io<TI>::load(k, chain * D + c);
-        s_a[c] = expf(g[chain * D + c]);
+        s_a[c] = expf(GateRow(g, g_head, chain, D).at(c));
     }
     __syncthreads();
     if (t < 64) {
@@ -106,7 +106,7 @@ hipError_t launch_t(const DecodeArgs &a) {
     const unsigned chains = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((decode_kernel<D, NT, W, TI, TB, TO>), dim3(chains * (D / W)), dim3(NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
-                       a.g, static_cast<const TB *>(a.beta), a.S, static_cast<TO *>(a.out));
+                       a.g, static_cast<const TB *>(a.beta), a.S, static_cast<TO *>(a.out), a.g_head);
     return hipGetLastError();
 }
 

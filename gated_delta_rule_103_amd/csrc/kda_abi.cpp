@@ -56,17 +56,19 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
                  const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B, int T,
                  int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
                  int snapshot_every, int max_snapshots, float *snapshots, void *workspace,
-                 size_t workspace_bytes, void *stream) {
-    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+                 size_t workspace_bytes, void *stream, bool g_head = false) {
+    // a per-head gate may be absent (no decay); a per-channel gate may not
+    if (!q || !k || !v || (!g && !g_head) || !beta || !out) return KDA_ERR_INVALID_ARG;
     if (N < 1 || B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || C < 1) return KDA_ERR_INVALID_ARG;
     if (!dtype_ok(io_dtype) || !dtype_ok(beta_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_INVALID_ARG;
     if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
     const long long T_total = (long long)B * T;
     if (T_total > INT_MAX / 2 || (long long)N * H > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
-    // q, k, v and g are read with 16-byte vector loads
+    // q, k, v and a per-channel g are read with 16-byte vector loads
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
-         reinterpret_cast<uintptr_t>(g)) & 15u)
+         (g_head ? 0u : reinterpret_cast<uintptr_t>(g))) & 15u)
         return KDA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(g) & 3u) return KDA_ERR_INVALID_ARG;
     if (snapshots) {
         if (snapshot_every < 1 || max_snapshots < 1) return KDA_ERR_INVALID_ARG;
         if ((long long)N * H * max_snapshots > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
@@ -86,6 +88,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     a.out_dt = static_cast<Dt>(out_dtype);
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
+    a.g_head = g_head;
     if (snapshots) {
         a.snaps = snapshots;
         a.snap_every = snapshot_every / C;
@@ -118,10 +121,23 @@ int kda_prefill_snapshots(const void *q, const void *k, const void *v, const flo
                         workspace_bytes, stream);
 }
 
-int kda_decode(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
-               void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
-               kda_dtype out_dtype, void *stream) {
-    if (!q || !k || !v || !g || !beta || !S || !out) return KDA_ERR_INVALID_ARG;
+int gdn_prefill(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B,
+                int T, int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
+                kda_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(q, k, v, g, beta, S0, out, S_out, cu_seqlens, N, B, T, H, Dk, Dv, C, io_dtype,
+                        beta_dtype, out_dtype, 0, 0, nullptr, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
+                void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
+                kda_dtype out_dtype, void *stream, bool g_head) {
+    if (!q || !k || !v || (!g && !g_head) || !beta || !S || !out) return KDA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(g) & 3u) return KDA_ERR_INVALID_ARG;
     if (N < 1 || H < 1 || Dk < 1 || Dv < 1) return KDA_ERR_INVALID_ARG;
     if (!dtype_ok(io_dtype) || !dtype_ok(beta_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_INVALID_ARG;
     if ((long long)N * H > INT_MAX) return KDA_ERR_INVALID_ARG;
@@ -132,7 +148,24 @@ int kda_decode(const void *q, const void *k, const void *v, const float *g, cons
     a.io = static_cast<Dt>(io_dtype); a.beta_dt = static_cast<Dt>(beta_dtype);
     a.out_dt = static_cast<Dt>(out_dtype);
     a.stream = static_cast<hipStream_t>(stream);
+    a.g_head = g_head;
     return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
+               void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
+               kda_dtype out_dtype, void *stream) {
+    return decode_impl(q, k, v, g, beta, S, out, N, H, Dk, Dv, io_dtype, beta_dtype, out_dtype, stream, false);
+}
+
+int gdn_decode(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
+               void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
+               kda_dtype out_dtype, void *stream) {
+    return decode_impl(q, k, v, g, beta, S, out, N, H, Dk, Dv, io_dtype, beta_dtype, out_dtype, stream, true);
 }
 
 }  // extern "C"

@@ -31,6 +31,28 @@ template <> struct io<bf16_t> {
     __device__ __forceinline__ static void store(bf16_t *p, size_t i, float x) { p[i] = f32_to_bf16(x); }
 };
 
+// Raw buffer access: a wave-uniform base and byte range held in scalar
+// registers, plus a 32-bit per-lane offset. A load past the range reads 0 and
+// a store past it is dropped; an empty range (base may be null) never touches
+// memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ float buf_ld_f32(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+// Log-decay gate of one chain (sequence or token row, head): per key channel,
+// g[row][h][0..D) (KDA); per head, g[row][h] broadcast over the channels (Gated
+// DeltaNet); or none, g == nullptr (DeltaNet, alpha = 1). row_h = row * H + h.
+struct GateRow {
+    __amdgpu_buffer_rsrc_t r;
+    bool per_head;
+    __device__ GateRow(const float *g, bool head, size_t row_h, int D)
+        : r(buf_rsrc(g ? g + (head ? row_h : row_h * D) : nullptr, g ? (head ? 4 : D * 4) : 0)), per_head(head) {}
+    __device__ float at(int c) const { return buf_ld_f32(r, per_head ? 0 : c * 4); }
+};
+
 __device__ __forceinline__ float warp_sum(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);

@@ -27,6 +27,10 @@ struct PrefillArgs {
     // snap_every chunks of each sequence (nullptr: none)
     float *snaps = nullptr;
     int snap_every = 0, max_snaps = 0;
+    // gate layout: false: g [T_total][H][Dk], one log-decay per key channel (KDA);
+    // true: g [T_total][H], one per head broadcast over the channels (Gated
+    // DeltaNet), and g == nullptr means no decay (DeltaNet)
+    bool g_head = false;
 };
 
 struct DecodeArgs {
@@ -38,6 +42,7 @@ struct DecodeArgs {
     int N, H, Dk, Dv;
     Dt io, beta_dt, out_dt;
     hipStream_t stream;
+    bool g_head = false;        // as in PrefillArgs: g [N][H] or nullptr
 };
 
 // Upper bound on the number of chunks of all sequences (each sequence adds at

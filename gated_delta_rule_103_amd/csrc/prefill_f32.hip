@@ -58,7 +58,7 @@ template <int C, int D, typename TI, typename TB>
 __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                    const TI *__restrict__ v, const float *__restrict__ g,
                                                    const TB *__restrict__ beta, SeqView sv, int H,
-                                                   float *__restrict__ rec_base) {
+                                                   float *__restrict__ rec_base, bool g_head) {
     using R = Rec<C, D>;
     __shared__ float s_a[C][D];
     __shared__ float s_L[C][C];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, con
     if (t < D) {
         float acc = 0.f;
         for (int tau = 0; tau < C; ++tau) {
-            if (tau < Lc) acc += g[row(tau) + t];
+            if (tau < Lc) acc += GateRow(g, g_head, (size_t)(s0 + tau) * H + h, D).at(t);
             s_a[tau][t] = acc;
         }
     }
@@ -223,7 +223,7 @@ hipError_t run(const PrefillArgs &a) {
     if (maxc > 0) {
         hipLaunchKernelGGL((prep_kernel<C, D, TI, TB>), dim3((unsigned)maxc, a.H), dim3(256), 0, a.stream,
                            static_cast<const TI *>(a.q), static_cast<const TI *>(a.k),
-                           static_cast<const TI *>(a.v), a.g, static_cast<const TB *>(a.beta), sv, a.H, recs);
+                           static_cast<const TI *>(a.v), a.g, static_cast<const TB *>(a.beta), sv, a.H, recs, a.g_head);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     (void)sizeof(R);

@@ -78,13 +78,8 @@ __device__ __forceinline__ bf16x8 lds8(const __bf16 *p) { return *reinterpret_ca
 __device__ __forceinline__ f16x8 lds8h(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 __device__ __forceinline__ float bf2f(__bf16 x) { return static_cast<float>(x); }
 
-// Raw buffer access: a wave-uniform base and byte range held in scalar
-// registers, plus a 32-bit per-lane offset. A load past the range reads 0 and
-// a store past it is dropped, so the ragged tail of a sequence needs no
-// branch, and no per-lane 64-bit address arithmetic is spent per access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-}
+// Raw buffer access (buf_rsrc): the ragged tail of a sequence needs no branch,
+// and no per-lane 64-bit address arithmetic is spent per access.
 template <typename T>
 __device__ __forceinline__ T buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -183,7 +178,9 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(SeqView sv, int2 *meta,
     meta[ci] = int2{tok0, min(C, sv.seq_end(n) - tok0)};
 }
 
-template <typename TB, bool VARLEN>
+// GHEAD: one log-decay per (token, head), g [T][H] or none (nullptr), instead
+// of one per key channel
+template <typename TB, bool VARLEN, bool GHEAD>
 __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
@@ -256,10 +253,22 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         if (part == -1 || part == 1) {
+            if constexpr (GHEAD) {
+                // one value per row, broadcast over the channels; without a gate the
+                // range is empty and every load reads 0 (alpha = 1)
+                const auto rgh = buf_rsrc(p.g ? p.g + (size_t)tok0 * H + h : nullptr, p.g ? ((Lc - 1) * H + 1) * 4 : 0);
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int idx = tid0 + it * PTHR, row = idx >> 5, part = idx & 31;
-                rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
+                for (int it = 0; it < 4; ++it) {
+                    const int row = (tid0 + it * PTHR) >> 5;
+                    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgh, min(row, Lc - 1) * H * 4, 0, 0));
+                    rg[it] = f32x4{x, x, x, x};
+                }
+            } else {
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int idx = tid0 + it * PTHR, row = idx >> 5, part = idx & 31;
+                    rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
+                }
             }
         }
         if (part == -1 || part == 2)
@@ -460,7 +469,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         for (int c = lane; c < D; c += 64) {
                             float lg = 0.f;
                             for (int rho = S_ + 1; rho <= T_; ++rho)
-                                lg += (rho < Lc) ? p.g[((size_t)(tok0 + rho) * H + h) * D + c] : 0.f;
+                                if (rho < Lc) lg += GateRow(p.g, GHEAD, (size_t)(tok0 + rho) * H + h, D).at(c);
                             const float w = expf(lg), kk = bf2f(sK[S_ * SQ + c]);
                             accl += bf2f(sK[T_ * SQ + c]) * kk * w;
                             accm += bf2f(sQ[T_ * SQ + c]) * kk * w;
@@ -935,13 +944,14 @@ hipError_t run(const PrefillArgs &a) {
         if (e != hipSuccess) return e;
     }
     {
-        auto kern = varlen ? chunk_prep_kernel<TB, true> : chunk_prep_kernel<TB, false>;
-        static bool attr[2] = {false, false};
-        if (!attr[varlen]) {
+        auto kern = varlen ? (a.g_head ? chunk_prep_kernel<TB, true, true> : chunk_prep_kernel<TB, true, false>)
+                           : (a.g_head ? chunk_prep_kernel<TB, false, true> : chunk_prep_kernel<TB, false, false>);
+        static bool attr[2][2] = {{false, false}, {false, false}};
+        if (!attr[varlen][a.g_head]) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
             if (e != hipSuccess) return e;
-            attr[varlen] = true;
+            attr[varlen][a.g_head] = true;
         }
         PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, meta,
                       a.H, recs, maxc};

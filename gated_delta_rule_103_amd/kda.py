@@ -55,6 +55,10 @@ def load_library() -> ctypes.CDLL:
                                           i, i, i, i, i, i, i, i, i, i, i, i, vp, vp, sz, vp]
     lib.kda_decode.restype = i
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.gdn_prefill.restype = i
+    lib.gdn_prefill.argtypes = lib.kda_prefill.argtypes
+    lib.gdn_decode.restype = i
+    lib.gdn_decode.argtypes = lib.kda_decode.argtypes
     _lib = lib
     return lib
 
@@ -100,21 +104,37 @@ def _prefill_buffers(lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, work
     return (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes
 
 
+def _prefill(entry, q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace, stream,
+             return_state):
+    lib = load_library()
+    (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
+        lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
+    st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
+                             _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
+                             _dt(out), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KDAError(st, entry)
+    return out, S_out
+
+
 def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
                 out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
                 return_state: bool = True):
     """Chunked KDA prefill. q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
     S0: [N, H, Dk, Dv] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B == 1) or None.
     Returns (out [B, T, H, Dv], S_out [N, H, Dk, Dv] or None)."""
-    lib = load_library()
-    (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
-        lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
-    st = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
-                         _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
-                         _dt(out), _ptr(workspace), ws_bytes, _stream(stream))
-    if st != 0:
-        raise KDAError(st, "kda_prefill")
-    return out, S_out
+    return _prefill("kda_prefill", q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace,
+                    stream, return_state)
+
+
+def gdn_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
+                out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
+                return_state: bool = True):
+    """Chunked prefill with the scalar gate of Gated DeltaNet: g [B, T, H] fp32 (one
+    log-decay per token and head), or None for DeltaNet (no decay). Otherwise as
+    kda_prefill."""
+    return _prefill("gdn_prefill", q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace,
+                    stream, return_state)
 
 
 def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max_snapshots: int,
@@ -139,17 +159,28 @@ def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max
     return out, S_out, snapshots
 
 
-def kda_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
-               stream=None):
-    """One decode step, state S [N, H, Dk, Dv] fp32 updated in place.
-    q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H]. Returns out [N, H, Dv]."""
+def _decode(entry, q, k, v, g, beta, S, out, out_dtype, stream):
     lib = load_library()
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     if out is None:
         out = torch.empty(N, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
-    st = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
-                        N, H, Dk, Dv, _dt(q), _dt(beta), _dt(out), _stream(stream))
+    st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
+                             N, H, Dk, Dv, _dt(q), _dt(beta), _dt(out), _stream(stream))
     if st != 0:
-        raise KDAError(st, "kda_decode")
+        raise KDAError(st, entry)
     return out
+
+
+def kda_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
+               stream=None):
+    """One decode step, state S [N, H, Dk, Dv] fp32 updated in place.
+    q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H]. Returns out [N, H, Dv]."""
+    return _decode("kda_decode", q, k, v, g, beta, S, out, out_dtype, stream)
+
+
+def gdn_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
+               stream=None):
+    """kda_decode with the scalar gate of Gated DeltaNet: g [N, H] fp32, or None
+    for DeltaNet (no decay)."""
+    return _decode("gdn_decode", q, k, v, g, beta, S, out, out_dtype, stream)

@@ -143,6 +143,26 @@ int kda_prefill_snapshots(const void *q, const void *k, const void *v, const flo
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill -- the same chunked prefill with the scalar forget gate of Gated
+ * DeltaNet, or with no gate (DeltaNet). Per the explainer's GDN/KDA paragraph,
+ * GDN applies one forget gate alpha to the whole state, which KDA refines into
+ * one decay per key channel; the DeltaNet section's delta rule is the case
+ * alpha = 1. The recurrence above holds with Diag(alpha_t) = alpha_t I.
+ *
+ * All arguments and the support matrix as for kda_prefill, except:
+ *   g   [B][T][H] fp32 (with cu_seqlens: [1][T_total][H]): the natural-log
+ *       decay of each token and head, alpha_t = exp(g_t) for every key channel;
+ *       or NULL: alpha_t = 1 (DeltaNet). 4-byte aligned; no 16-byte rule.
+ * kda_prefill_workspace_size gives the workspace. The kernels are kda_prefill's,
+ * reading one decay per token and head.
+ */
+int gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                const void *beta, const float *S0, void *out, float *S_out,
+                const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_decode -- one token per sequence, state updated in place. This is one
  * step of the recurrence above (the explainer's decode paragraph: about
  * 7*D^2 FLOPs and about 8*D^2 bytes per head, the fp32 state being read and
@@ -156,6 +176,15 @@ int kda_prefill_snapshots(const void *q, const void *k, const void *v, const flo
  * and out_dtype either; N*H >= 1.
  */
 int kda_decode(const void *q, const void *k, const void *v, const float *g,
+               const void *beta, float *S, void *out, int N, int H, int Dk, int Dv,
+               kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype, void *stream);
+
+/*
+ * gdn_decode -- kda_decode with the scalar gate of Gated DeltaNet (g [N][H]
+ * fp32, alpha = exp(g) for every key channel) or none (g NULL: DeltaNet,
+ * alpha = 1). Otherwise as kda_decode.
+ */
+int gdn_decode(const void *q, const void *k, const void *v, const float *g,
                const void *beta, float *S, void *out, int N, int H, int Dk, int Dv,
                kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype, void *stream);
 

@@ -41,13 +41,13 @@ def test_status_strings(lib):
     assert lib.kda_status_string(99) == b"KDA_UNKNOWN_STATUS"
 
 
-def _prefill(lib, **kw):
+def _prefill(lib, entry="kda_prefill", **kw):
     fake = ctypes.c_void_p(256)          # never dereferenced: checks return first
     a = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, S0=None, out=fake, S_out=None,
              cu=None, N=1, B=1, T=64, H=2, Dk=64, Dv=64, C=16, io=1, bd=1, od=1,
              ws=None, wsb=0, stream=None)
     a.update(kw)
-    return lib.kda_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["out"], a["S_out"],
+    return getattr(lib, entry)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["out"], a["S_out"],
                            a["cu"], a["N"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["C"],
                            a["io"], a["bd"], a["od"], a["ws"], a["wsb"], a["stream"])
 
@@ -105,12 +105,12 @@ def test_workspace_size_is_pure_and_rejects_bad_sizes(lib):
     assert lib.kda_prefill_workspace_size(1, 100, 2, 64, 64, 12, 1) == 0
 
 
-def _decode(lib, **kw):
+def _decode(lib, entry="kda_decode", **kw):
     fake = ctypes.c_void_p(256)
     a = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, S=fake, out=fake, N=4, H=2, Dk=128,
              Dv=128, io=1, bd=1, od=1, stream=None)
     a.update(kw)
-    return lib.kda_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["out"], a["N"],
+    return getattr(lib, entry)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["out"], a["N"],
                           a["H"], a["Dk"], a["Dv"], a["io"], a["bd"], a["od"], a["stream"])
 
 
@@ -120,6 +120,25 @@ def _decode(lib, **kw):
 ])
 def test_decode_argument_errors(lib, kw, status):
     assert _decode(lib, **kw) == status
+
+
+# gdn_prefill / gdn_decode: a NULL gate is allowed (DeltaNet), so these cases reach
+# the later checks; a per-head gate needs 4-byte, not 16-byte, alignment
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None, N=0), -1), (dict(g=None, Dk=96, Dv=96), -2), (dict(g=None, q=None), -1),
+    (dict(g=ctypes.c_void_p(258)), -1), (dict(g=ctypes.c_void_p(260), C=8), -2),
+    (dict(g=None, ws=None, wsb=0, io=0, bd=0, od=0), -3),
+])
+def test_gdn_prefill_argument_errors(lib, kw, status):
+    assert _prefill(lib, "gdn_prefill", **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=None, Dk=32, Dv=32), -2), (dict(g=None, S=None), -1), (dict(g=ctypes.c_void_p(258)), -1),
+    (dict(g=ctypes.c_void_p(260), N=0), -1),
+])
+def test_gdn_decode_argument_errors(lib, kw, status):
+    assert _decode(lib, "gdn_decode", **kw) == status
 
 
 def test_cost_models_match_the_pages():
