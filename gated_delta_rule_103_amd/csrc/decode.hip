@@ -24,7 +24,7 @@ template <int D, int NT, int W, typename TI, typename TB, typename TO>
 __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                     const TI *__restrict__ v, const float *__restrict__ g,
                                                     const TB *__restrict__ beta, float *__restrict__ S,
-                                                    TO *__restrict__ out, bool g_head) {
+                                                    TO *__restrict__ out, bool g_head, bool qk_norm, float norm_eps) {
     // NT threads cover W columns of one chain: the reductions over key rows stay
     // inside the workgroup, so the columns of a chain are split over D / W
     // workgroups.
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, co
     static_assert(CG * RG == NT && RG * RPT == D, "decode tiling");
     __shared__ float s_q[D], s_k[D], s_a[D], s_u[W];
     __shared__ float s_red[2][RG][W];
-    __shared__ float s_qk;
+    __shared__ float s_qk, s_nq, s_nk;
 
     constexpr int SPLIT = D / W;
     const size_t chain = blockIdx.x / SPLIT;
@@ -54,17 +54,36 @@ __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, co
     }
     __syncthreads();
     if (t < 64) {
-        float x = 0.f;
-        for (int c = t; c < D; c += 64) x += s_q[c] * s_k[c];
+        float x = 0.f, xq = 0.f, xk = 0.f;
+        for (int c = t; c < D; c += 64) {
+            x += s_q[c] * s_k[c];
+            xq += s_q[c] * s_q[c];
+            xk += s_k[c] * s_k[c];
+        }
         x = warp_sum(x);
-        if (t == 0) s_qk = x;
+        xq = warp_sum(xq);
+        xk = warp_sum(xk);
+        if (t == 0) {
+            // L2-normalised q and k: x / sqrt(sum x^2 + eps), applied as two scalars
+            const float nq = qk_norm ? 1.f / sqrtf(xq + norm_eps) : 1.f;
+            const float nk = qk_norm ? 1.f / sqrtf(xk + norm_eps) : 1.f;
+            s_qk = x * nq * nk;
+            s_nq = nq;
+            s_nk = nk;
+        }
+    }
+    float nq = 1.f, nk = 1.f;
+    if (qk_norm) {                                     // uniform
+        __syncthreads();
+        nq = s_nq;
+        nk = s_nk;
     }
 
     float4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        const float a = s_a[r], kr = s_k[r], qr = s_q[r];
+        const float a = s_a[r], kr = s_k[r] * nk, qr = s_q[r] * nq;
         m[i].x *= a; m[i].y *= a; m[i].z *= a; m[i].w *= a;
         pk.x += kr * m[i].x; pk.y += kr * m[i].y; pk.z += kr * m[i].z; pk.w += kr * m[i].w;
         pq.x += qr * m[i].x; pq.y += qr * m[i].y; pq.z += qr * m[i].z; pq.w += qr * m[i].w;
@@ -86,7 +105,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, co
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        const float kr = s_k[r];
+        const float kr = s_k[r] * nk;
         f32x4 x = m[i];
         x.x += kr * u4.x; x.y += kr * u4.y; x.z += kr * u4.z; x.w += kr * u4.w;
         __builtin_nontemporal_store(x, &Sp[r * (D / 4) + cg]);
@@ -106,7 +125,8 @@ hipError_t launch_t(const DecodeArgs &a) {
     const unsigned chains = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((decode_kernel<D, NT, W, TI, TB, TO>), dim3(chains * (D / W)), dim3(NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
-                       a.g, static_cast<const TB *>(a.beta), a.S, static_cast<TO *>(a.out), a.g_head);
+                       a.g, static_cast<const TB *>(a.beta), a.S, static_cast<TO *>(a.out), a.g_head, a.qk_norm,
+                       a.norm_eps);
     return hipGetLastError();
 }
 

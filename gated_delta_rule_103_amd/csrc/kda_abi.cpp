@@ -25,6 +25,14 @@ size_t workspace_for(int N, long long T_total, int H, int Dk, int Dv, int C, kda
                         : kda::prefill_f32_workspace(N, T_total, H, Dk, Dv, C);
 }
 
+// options: NULL = defaults; a bad gate or a norm without eps > 0 is an argument error
+bool options_ok(const kda_options *o) {
+    if (!o) return true;
+    if (o->gate != KDA_GATE_CHANNEL && o->gate != KDA_GATE_HEAD) return false;
+    if (o->qk_l2norm && !(o->l2norm_eps > 0.f)) return false;      // also rejects NaN
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,7 +64,8 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
                  const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B, int T,
                  int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
                  int snapshot_every, int max_snapshots, float *snapshots, void *workspace,
-                 size_t workspace_bytes, void *stream, bool g_head = false) {
+                 size_t workspace_bytes, void *stream, bool g_head = false, bool qk_norm = false,
+                 float norm_eps = 0.f) {
     // a per-head gate may be absent (no decay); a per-channel gate may not
     if (!q || !k || !v || (!g && !g_head) || !beta || !out) return KDA_ERR_INVALID_ARG;
     if (N < 1 || B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || C < 1) return KDA_ERR_INVALID_ARG;
@@ -89,6 +98,8 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
     a.g_head = g_head;
+    a.qk_norm = qk_norm;
+    a.norm_eps = norm_eps;
     if (snapshots) {
         a.snaps = snapshots;
         a.snap_every = snapshot_every / C;
@@ -135,7 +146,7 @@ namespace {
 
 int decode_impl(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
                 void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
-                kda_dtype out_dtype, void *stream, bool g_head) {
+                kda_dtype out_dtype, void *stream, bool g_head, bool qk_norm = false, float norm_eps = 0.f) {
     if (!q || !k || !v || (!g && !g_head) || !beta || !S || !out) return KDA_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(g) & 3u) return KDA_ERR_INVALID_ARG;
     if (N < 1 || H < 1 || Dk < 1 || Dv < 1) return KDA_ERR_INVALID_ARG;
@@ -149,6 +160,8 @@ int decode_impl(const void *q, const void *k, const void *v, const float *g, con
     a.out_dt = static_cast<Dt>(out_dtype);
     a.stream = static_cast<hipStream_t>(stream);
     a.g_head = g_head;
+    a.qk_norm = qk_norm;
+    a.norm_eps = norm_eps;
     return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -166,6 +179,34 @@ int gdn_decode(const void *q, const void *k, const void *v, const float *g, cons
                void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
                kda_dtype out_dtype, void *stream) {
     return decode_impl(q, k, v, g, beta, S, out, N, H, Dk, Dv, io_dtype, beta_dtype, out_dtype, stream, true);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int kda_prefill_ex(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                   const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B, int T,
+                   int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
+                   kda_dtype out_dtype, const kda_options *opt, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (!options_ok(opt)) return KDA_ERR_INVALID_ARG;
+    const kda_options o = opt ? *opt : kda_options{};
+    if (o.snapshots && (o.snapshot_every < 1 || o.max_snapshots < 1)) return KDA_ERR_INVALID_ARG;
+    return prefill_impl(q, k, v, g, beta, S0, out, S_out, cu_seqlens, N, B, T, H, Dk, Dv, C, io_dtype,
+                        beta_dtype, out_dtype, o.snapshots ? o.snapshot_every : 0,
+                        o.snapshots ? o.max_snapshots : 0, o.snapshots, workspace, workspace_bytes, stream,
+                        o.gate == KDA_GATE_HEAD, o.qk_l2norm != 0, o.l2norm_eps);
+}
+
+int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, const void *beta, float *S,
+                  void *out, int N, int H, int Dk, int Dv, kda_dtype io_dtype, kda_dtype beta_dtype,
+                  kda_dtype out_dtype, const kda_options *opt, void *stream) {
+    if (!options_ok(opt)) return KDA_ERR_INVALID_ARG;
+    const kda_options o = opt ? *opt : kda_options{};
+    if (o.snapshots) return KDA_ERR_INVALID_ARG;                  // prefill only
+    return decode_impl(q, k, v, g, beta, S, out, N, H, Dk, Dv, io_dtype, beta_dtype, out_dtype, stream,
+                       o.gate == KDA_GATE_HEAD, o.qk_l2norm != 0, o.l2norm_eps);
 }
 
 }  // extern "C"

@@ -31,6 +31,9 @@ struct PrefillArgs {
     // true: g [T_total][H], one per head broadcast over the channels (Gated
     // DeltaNet), and g == nullptr means no decay (DeltaNet)
     bool g_head = false;
+    // L2-normalise q and k over Dk inside the kernels: x / sqrt(sum x^2 + norm_eps)
+    bool qk_norm = false;
+    float norm_eps = 0.f;
 };
 
 struct DecodeArgs {
@@ -43,6 +46,8 @@ struct DecodeArgs {
     Dt io, beta_dt, out_dt;
     hipStream_t stream;
     bool g_head = false;        // as in PrefillArgs: g [N][H] or nullptr
+    bool qk_norm = false;       // as in PrefillArgs
+    float norm_eps = 0.f;
 };
 
 // Upper bound on the number of chunks of all sequences (each sequence adds at

@@ -58,12 +58,14 @@ template <int C, int D, typename TI, typename TB>
 __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                    const TI *__restrict__ v, const float *__restrict__ g,
                                                    const TB *__restrict__ beta, SeqView sv, int H,
-                                                   float *__restrict__ rec_base, bool g_head) {
+                                                   float *__restrict__ rec_base, bool g_head, bool qk_norm,
+                                                   float norm_eps) {
     using R = Rec<C, D>;
     __shared__ float s_a[C][D];
     __shared__ float s_L[C][C];
     __shared__ float s_inv[C][C];
     __shared__ float s_beta[C];
+    __shared__ float s_rq[C], s_rk[C];   // 1 / ||q_t||, 1 / ||k_t|| when q and k are L2-normalised, else 1
 
     const int ci = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     if (ci >= sv.total_chunks()) return;
@@ -83,6 +85,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, con
         }
     }
     if (t < C) s_beta[t] = t < Lc ? io<TB>::load(beta, (size_t)(s0 + t) * H + h) : 0.f;
+    if (t < C) {
+        float sq = 0.f, sk = 0.f;
+        if (qk_norm && t < Lc)
+            for (int c = 0; c < D; ++c) {
+                const float a = io<TI>::load(q, row(t) + c), b = io<TI>::load(k, row(t) + c);
+                sq += a * a;
+                sk += b * b;
+            }
+        s_rq[t] = qk_norm && t < Lc ? 1.f / sqrtf(sq + norm_eps) : 1.f;
+        s_rk[t] = qk_norm && t < Lc ? 1.f / sqrtf(sk + norm_eps) : 1.f;
+    }
     __syncthreads();
 
     // Mqk (to the record) and L (to LDS), exact per-element exponentials
@@ -97,6 +110,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, con
                 lk += io<TI>::load(k, row(tau) + c) * ks * e;
             }
         }
+        mq *= s_rq[tau] * s_rk[sig];
+        lk *= s_rk[tau] * s_rk[sig];
         rec[R::MQK + p] = mq;
         s_L[tau][sig] = sig < tau ? s_beta[tau] * lk : 0.f;
     }
@@ -119,8 +134,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, con
         const int tau = p / D, c = p % D;
         float qd = 0.f, kr = 0.f;
         if (tau < Lc) {
-            qd = io<TI>::load(q, row(tau) + c) * expf(s_a[tau][c]);
-            kr = io<TI>::load(k, row(tau) + c) * expf(s_a[C - 1][c] - s_a[tau][c]);
+            qd = io<TI>::load(q, row(tau) + c) * s_rq[tau] * expf(s_a[tau][c]);
+            kr = io<TI>::load(k, row(tau) + c) * s_rk[tau] * expf(s_a[C - 1][c] - s_a[tau][c]);
         }
         rec[R::QD + p] = qd;
         rec[R::KR + p] = kr;
@@ -134,7 +149,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI *__restrict__ q, con
         if (tau < Lc) {
             for (int sig = 0; sig <= tau; ++sig) {
                 const float ib = s_inv[tau][sig] * s_beta[sig];
-                w += ib * io<TI>::load(k, row(sig) + c) * expf(s_a[sig][c]);
+                w += ib * io<TI>::load(k, row(sig) + c) * s_rk[sig] * expf(s_a[sig][c]);
                 ut += ib * io<TI>::load(v, row(sig) + c);
             }
         }
@@ -223,7 +238,8 @@ hipError_t run(const PrefillArgs &a) {
     if (maxc > 0) {
         hipLaunchKernelGGL((prep_kernel<C, D, TI, TB>), dim3((unsigned)maxc, a.H), dim3(256), 0, a.stream,
                            static_cast<const TI *>(a.q), static_cast<const TI *>(a.k),
-                           static_cast<const TI *>(a.v), a.g, static_cast<const TB *>(a.beta), sv, a.H, recs, a.g_head);
+                           static_cast<const TI *>(a.v), a.g, static_cast<const TB *>(a.beta), sv, a.H, recs, a.g_head, a.qk_norm,
+                           a.norm_eps);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     (void)sizeof(R);

@@ -152,7 +152,9 @@ struct PrepLds {
     static constexpr int G = GB + 4 * D * 4;         // fp32 [4][128] decay chunk start -> block start
     static constexpr int H = G + 4 * D * 4;          // fp32 [4][128] decay block end -> chunk end
     static constexpr int GAM = H + 4 * D * 4;        // fp32 [128]
-    static constexpr int FLAG = GAM + D * 4;         // int [4]
+    static constexpr int RQ = GAM + D * 4;           // fp32 [64] 1 / ||q_t|| (L2-normalised input)
+    static constexpr int RK = RQ + C * 4;            // fp32 [64] 1 / ||k_t||
+    static constexpr int FLAG = RK + C * 4;          // int [4]
     static constexpr int T3 = FLAG + 16;             // fp32 [3][256] inverse scratch
     static constexpr int SIZE = T3 + 3 * 256 * 4;
 };
@@ -166,6 +168,7 @@ struct PrepParams {
     int H;
     char *rec;
     long long rec_stride;        // records per head (head-major record layout)
+    float norm_eps;              // NORM: q_t / sqrt(||q_t||^2 + eps), the same for k_t
 };
 
 // {first token, length} of every chunk of packed sequences (zeros past the last)
@@ -179,8 +182,10 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(SeqView sv, int2 *meta,
 }
 
 // GHEAD: one log-decay per (token, head), g [T][H] or none (nullptr), instead
-// of one per key channel
-template <typename TB, bool VARLEN, bool GHEAD>
+// of one per key channel. NORM: q and k are L2-normalised over the channels on
+// the fly: the staged rows stay the bf16 inputs, and 1/||q_t||, 1/||k_t|| (fp32)
+// scale every product they enter before its operands are rounded.
+template <typename TB, bool VARLEN, bool GHEAD, bool NORM>
 __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
@@ -197,6 +202,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     float *sG = reinterpret_cast<float *>(smem + Lo::G);
     float *sH = reinterpret_cast<float *>(smem + Lo::H);
     float *sGam = reinterpret_cast<float *>(smem + Lo::GAM);
+    float *sRQ = reinterpret_cast<float *>(smem + Lo::RQ);
+    float *sRK = reinterpret_cast<float *>(smem + Lo::RK);
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
     float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
 
@@ -293,6 +300,25 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const u32x4 z0 = {0u, 0u, 0u, 0u};
             *reinterpret_cast<u32x4 *>(sQ + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
             *reinterpret_cast<u32x4 *>(sK + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
+            if constexpr (NORM) {
+                // sums of squares over the 16 threads of the row (lanes 16j..16j+15)
+                const bf16x8 qx = __builtin_bit_cast(bf16x8, rq[it]), kx = __builtin_bit_cast(bf16x8, rk[it]);
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sq += bf2f(qx[e]) * bf2f(qx[e]);
+                    sk += bf2f(kx[e]) * bf2f(kx[e]);
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    sq += __shfl_xor(sq, o, 64);
+                    sk += __shfl_xor(sk, o, 64);
+                }
+                if (part == 0) {
+                    sRQ[row] = row < Lc ? 1.f / sqrtf(sq + p.norm_eps) : 1.f;
+                    sRK[row] = row < Lc ? 1.f / sqrtf(sk + p.norm_eps) : 1.f;
+                }
+            }
         }
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -341,6 +367,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             acc += __shfl_xor(acc, 1, 64);
             acc += __shfl_xor(acc, 2, 64);
             acc += __shfl_xor(acc, 4, 64);
+            if constexpr (NORM) acc *= sRQ[row] * sRK[row];
             if (seg == 0) sDg[row] = acc;
         }
         // zero the upper blocks of Mqk (never written below)
@@ -376,6 +403,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const int I = wave;
             if (!sFlag[I]) {
                 const int t = 16 * I + l16;
+                const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
                 f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
@@ -388,10 +416,11 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float ee = e < 4 ? e0[e] : e1[e - 4];
-                        const float kk = bf2f(kv[e]);
+                        const float kk = NORM ? bf2f(kv[e]) * nk : bf2f(kv[e]);
+                        const float qq = NORM ? bf2f(qv[e]) * nq : bf2f(qv[e]);
                         const float bk = kk * __builtin_amdgcn_rcpf(ee);
                         accL = __builtin_amdgcn_mfma_f32_16x16x4f32(kk * ee, bk, accL, 0, 0, 0);
-                        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(bf2f(qv[e]) * ee, bk, accM, 0, 0, 0);
+                        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(qq * ee, bk, accM, 0, 0, 0);
                     }
                 }
 #pragma unroll
@@ -411,6 +440,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) { accL[bb] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[bb] = accL[bb]; }
             const int t = 16 * I + l16;
+            const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int c0 = 32 * ks + 8 * lq;
@@ -421,8 +451,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float fa = e < 4 ? a0[e] : a1[e - 4];
-                    aq[e] = static_cast<_Float16>(bf2f(qv[e]) * fa);
-                    ak[e] = static_cast<_Float16>(bf2f(kv[e]) * fa);
+                    aq[e] = static_cast<_Float16>(NORM ? bf2f(qv[e]) * nq * fa : bf2f(qv[e]) * fa);
+                    ak[e] = static_cast<_Float16>(NORM ? bf2f(kv[e]) * nk * fa : bf2f(kv[e]) * fa);
                 }
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {
@@ -439,9 +469,11 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     const f32x4 c0v = *reinterpret_cast<const f32x4 *>(gB), c1v = *reinterpret_cast<const f32x4 *>(gB + 4);
                     b0 *= (I - J >= 2 ? a0v : one) * (I - J == 3 ? c0v : one);
                     b1 *= (I - J >= 2 ? a1v : one) * (I - J == 3 ? c1v : one);
+                    const float ns = NORM ? sRK[sr] : 1.f;
                     f16x8 bk;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bk[e] = static_cast<_Float16>(bf2f(sv[e]) * (e < 4 ? b0[e] : b1[e - 4]));
+                    for (int e = 0; e < 8; ++e)
+                        bk[e] = static_cast<_Float16>((NORM ? bf2f(sv[e]) * ns : bf2f(sv[e])) * (e < 4 ? b0[e] : b1[e - 4]));
                     accL[bb] = mfma_f16(ak, bk, accL[bb]);
                     accM[bb] = mfma_f16(aq, bk, accM[bb]);
                 }
@@ -476,6 +508,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         }
                         accl = warp_sum(accl);
                         accm = warp_sum(accm);
+                        if constexpr (NORM) {
+                            accl *= sRK[T_] * sRK[S_];
+                            accm *= sRQ[T_] * sRK[S_];
+                        }
                         if (lane == 0) {
                             sLI[T_ * SL + S_] = sBeta[T_] * accl;
                             sMqk[T_ * SMQ + S_] = static_cast<_Float16>(accm);
@@ -554,6 +590,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             f16x8 fr[8];
             if (wave < 4) {
                 const int I = role;
+                const float nqr = NORM ? sRQ[t] : 1.f, nkr = NORM ? sRK[t] : 1.f;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c0 = 32 * ks + 8 * lq;
@@ -565,8 +602,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
-                        fr[ks][e] = static_cast<_Float16>(bf2f(kx[e]) * dec);
-                        fr[4 + ks][e] = static_cast<_Float16>(bf2f(qx[e]) * dec);
+                        fr[ks][e] = static_cast<_Float16>((NORM ? bf2f(kx[e]) * nkr : bf2f(kx[e])) * dec);
+                        fr[4 + ks][e] = static_cast<_Float16>((NORM ? bf2f(qx[e]) * nqr : bf2f(qx[e])) * dec);
                     }
                 }
             } else {
@@ -577,10 +614,17 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     for (int ks = 0; ks < 2; ++ks) {
                         // tokens 32ks + 8lq .. +7 lie in one 16-token block
                         const float hb = sH[(2 * ks + (lq >> 1)) * D + chn];
+                        f32x4 n0 = {1.f, 1.f, 1.f, 1.f}, n1 = n0;
+                        if constexpr (NORM) {
+                            n0 = *reinterpret_cast<const f32x4 *>(sRK + 32 * ks + 8 * lq);
+                            n1 = *reinterpret_cast<const f32x4 *>(sRK + 32 * ks + 8 * lq + 4);
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int tt = 32 * ks + 8 * lq + e;
-                            fr[rt * 2 + ks][e] = static_cast<_Float16>(bf2f(sK[tt * SQ + chn]) * sF[tt * SE + chn] * hb);
+                            const float kk = NORM ? bf2f(sK[tt * SQ + chn]) * (e < 4 ? n0[e] : n1[e - 4])
+                                                  : bf2f(sK[tt * SQ + chn]);
+                            fr[rt * 2 + ks][e] = static_cast<_Float16>(kk * sF[tt * SE + chn] * hb);
                         }
                     }
                 }
@@ -944,17 +988,23 @@ hipError_t run(const PrefillArgs &a) {
         if (e != hipSuccess) return e;
     }
     {
-        auto kern = varlen ? (a.g_head ? chunk_prep_kernel<TB, true, true> : chunk_prep_kernel<TB, true, false>)
-                           : (a.g_head ? chunk_prep_kernel<TB, false, true> : chunk_prep_kernel<TB, false, false>);
-        static bool attr[2][2] = {{false, false}, {false, false}};
-        if (!attr[varlen][a.g_head]) {
+        // kernel variant [varlen][per-head gate][L2-normalised q, k]
+        using Kern = void (*)(PrepParams);
+        static const Kern kerns[2][2][2] = {
+            {{chunk_prep_kernel<TB, false, false, false>, chunk_prep_kernel<TB, false, false, true>},
+             {chunk_prep_kernel<TB, false, true, false>, chunk_prep_kernel<TB, false, true, true>}},
+            {{chunk_prep_kernel<TB, true, false, false>, chunk_prep_kernel<TB, true, false, true>},
+             {chunk_prep_kernel<TB, true, true, false>, chunk_prep_kernel<TB, true, true, true>}}};
+        static bool attr[2][2][2] = {};
+        const Kern kern = kerns[varlen][a.g_head][a.qk_norm];
+        if (!attr[varlen][a.g_head][a.qk_norm]) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
             if (e != hipSuccess) return e;
-            attr[varlen][a.g_head] = true;
+            attr[varlen][a.g_head][a.qk_norm] = true;
         }
         PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, meta,
-                      a.H, recs, maxc};
+                      a.H, recs, maxc, a.norm_eps};
         // persistent: one workgroup per CU walks the (chunk, head) items
         const long long items = maxc * a.H;
         const unsigned grid = (unsigned)std::min<long long>(items, prep_grid());

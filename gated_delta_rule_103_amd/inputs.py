@@ -78,12 +78,16 @@ def prefill(H: int, D: int, *, B: int = 1, T: Optional[int] = None,
             lengths: Optional[List[int]] = None, C: int = 64, io: str = "bf16",
             beta_io: Optional[str] = None, shift: float = 2.0, gate: str = "softplus",
             s0_std: Optional[float] = None, seed: int = 0, device="cpu",
-            v_zero: bool = False, beta_one: bool = False, Dv: Optional[int] = None) -> PrefillInputs:
+            v_zero: bool = False, beta_one: bool = False, Dv: Optional[int] = None,
+            qk_scale: Optional[tuple] = None) -> PrefillInputs:
     """Draw one prefill problem.
 
     Either dense ``(B, T)`` or packed ``lengths`` (then B = 1 and cu_seqlens is
     returned). ``gate``: "softplus" -> g = -softplus(N + shift); "zero" -> g = 0
     (alpha = 1); "slow" -> g = -softplus(N - 4) (alpha ~ 0.97).
+    ``qk_scale=(lo, hi)``: q and k rows are multiplied by factors drawn from
+    U[lo, hi] before rounding (inputs for the fused L2 normalisation; drawn
+    last, so the other tensors are those of the same seed without it).
     """
     dev = torch.device(device)
     gen = _gen(seed, dev)
@@ -118,6 +122,11 @@ def prefill(H: int, D: int, *, B: int = 1, T: Optional[int] = None,
         v = torch.zeros_like(v)
     if beta_one:
         beta = torch.ones_like(beta)
+    if qk_scale is not None:
+        lo, hi = qk_scale
+        u = lambda: lo + (hi - lo) * torch.rand(B, T, H, 1, generator=gen, device=dev, dtype=torch.float32)
+        q = (q.float() * u()).to(dt)
+        k = (k.float() * u()).to(dt)
     return PrefillInputs(q, k, v, g.contiguous(), beta, S0, cu, C,
                          meta=dict(H=H, Dk=Dk, Dv=Dv, B=B, T=T, io=io, seed=seed,
                                    gate=gate, shift=shift, lengths=lengths))
@@ -153,7 +162,7 @@ class DecodeInputs:
 
 def decode(N: int, H: int, D: int, steps: int, *, io: str = "bf16", shift: float = 2.0,
            gate: str = "softplus", state_std: float = 0.02, seed: int = 0,
-           device="cpu") -> DecodeInputs:
+           device="cpu", qk_scale: Optional[tuple] = None) -> DecodeInputs:
     dev = torch.device(device)
     gen = _gen(seed, dev)
     dt = _DT[io]
@@ -172,6 +181,11 @@ def decode(N: int, H: int, D: int, steps: int, *, io: str = "bf16", shift: float
     else:
         raise ValueError(gate)
     beta = torch.sigmoid(rn(steps, N, H)).to(dt)
+    if qk_scale is not None:                 # as in prefill(): drawn last
+        lo, hi = qk_scale
+        u = lambda: lo + (hi - lo) * torch.rand(steps, N, H, 1, generator=gen, device=dev, dtype=torch.float32)
+        q = (q.float() * u()).to(dt)
+        k = (k.float() * u()).to(dt)
     return DecodeInputs(q, k, v, g.contiguous(), beta, state)
 
 

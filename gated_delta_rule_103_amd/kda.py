@@ -31,6 +31,16 @@ class KDAError(RuntimeError):
         self.status = status
 
 
+class Options(ctypes.Structure):
+    """kda_options of include/kda.h."""
+    _fields_ = [("gate", ctypes.c_int), ("qk_l2norm", ctypes.c_int), ("l2norm_eps", ctypes.c_float),
+                ("snapshot_every", ctypes.c_int), ("max_snapshots", ctypes.c_int),
+                ("snapshots", ctypes.c_void_p)]
+
+
+GATE_CHANNEL, GATE_HEAD = 0, 1
+
+
 def load_library() -> ctypes.CDLL:
     """Load libkda.so from the package directory (built by ``__graft_entry__.build()``)."""
     global _lib
@@ -59,6 +69,12 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_prefill.argtypes = lib.kda_prefill.argtypes
     lib.gdn_decode.restype = i
     lib.gdn_decode.argtypes = lib.kda_decode.argtypes
+    op = ctypes.POINTER(Options)
+    lib.kda_prefill_ex.restype = i
+    lib.kda_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   i, i, i, i, i, i, i, i, i, i, op, vp, sz, vp]
+    lib.kda_decode_ex.restype = i
+    lib.kda_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, op, vp]
     _lib = lib
     return lib
 
@@ -105,13 +121,19 @@ def _prefill_buffers(lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, work
 
 
 def _prefill(entry, q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace, stream,
-             return_state):
+             return_state, qk_l2norm=False, l2norm_eps=1e-6):
     lib = load_library()
     (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
         lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
-    st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
-                             _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
-                             _dt(out), _ptr(workspace), ws_bytes, _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_out),
+            _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta), _dt(out))
+    if qk_l2norm:
+        opt = Options(gate=GATE_HEAD if entry == "gdn_prefill" else GATE_CHANNEL, qk_l2norm=1,
+                      l2norm_eps=l2norm_eps)
+        entry = "kda_prefill_ex"
+        st = lib.kda_prefill_ex(*args, ctypes.byref(opt), _ptr(workspace), ws_bytes, _stream(stream))
+    else:
+        st = getattr(lib, entry)(*args, _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise KDAError(st, entry)
     return out, S_out
@@ -119,22 +141,23 @@ def _prefill(entry, q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, 
 
 def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
                 out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
-                return_state: bool = True):
+                return_state: bool = True, qk_l2norm: bool = False, l2norm_eps: float = 1e-6):
     """Chunked KDA prefill. q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
     S0: [N, H, Dk, Dv] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B == 1) or None.
+    qk_l2norm: L2-normalise q and k over Dk inside the kernels (x / sqrt(sum x^2 + eps)).
     Returns (out [B, T, H, Dv], S_out [N, H, Dk, Dv] or None)."""
     return _prefill("kda_prefill", q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace,
-                    stream, return_state)
+                    stream, return_state, qk_l2norm, l2norm_eps)
 
 
 def gdn_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
                 out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
-                return_state: bool = True):
+                return_state: bool = True, qk_l2norm: bool = False, l2norm_eps: float = 1e-6):
     """Chunked prefill with the scalar gate of Gated DeltaNet: g [B, T, H] fp32 (one
     log-decay per token and head), or None for DeltaNet (no decay). Otherwise as
     kda_prefill."""
     return _prefill("gdn_prefill", q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace,
-                    stream, return_state)
+                    stream, return_state, qk_l2norm, l2norm_eps)
 
 
 def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max_snapshots: int,
@@ -159,28 +182,35 @@ def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max
     return out, S_out, snapshots
 
 
-def _decode(entry, q, k, v, g, beta, S, out, out_dtype, stream):
+def _decode(entry, q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm=False, l2norm_eps=1e-6):
     lib = load_library()
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     if out is None:
         out = torch.empty(N, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
-    st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
-                             N, H, Dk, Dv, _dt(q), _dt(beta), _dt(out), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out), N, H, Dk, Dv, _dt(q),
+            _dt(beta), _dt(out))
+    if qk_l2norm:
+        opt = Options(gate=GATE_HEAD if entry == "gdn_decode" else GATE_CHANNEL, qk_l2norm=1,
+                      l2norm_eps=l2norm_eps)
+        entry = "kda_decode_ex"
+        st = lib.kda_decode_ex(*args, ctypes.byref(opt), _stream(stream))
+    else:
+        st = getattr(lib, entry)(*args, _stream(stream))
     if st != 0:
         raise KDAError(st, entry)
     return out
 
 
 def kda_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
-               stream=None):
+               stream=None, qk_l2norm: bool = False, l2norm_eps: float = 1e-6):
     """One decode step, state S [N, H, Dk, Dv] fp32 updated in place.
     q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H]. Returns out [N, H, Dv]."""
-    return _decode("kda_decode", q, k, v, g, beta, S, out, out_dtype, stream)
+    return _decode("kda_decode", q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm, l2norm_eps)
 
 
 def gdn_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
-               stream=None):
+               stream=None, qk_l2norm: bool = False, l2norm_eps: float = 1e-6):
     """kda_decode with the scalar gate of Gated DeltaNet: g [N, H] fp32, or None
     for DeltaNet (no decay)."""
-    return _decode("gdn_decode", q, k, v, g, beta, S, out, out_dtype, stream)
+    return _decode("gdn_decode", q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm, l2norm_eps)

@@ -56,6 +56,35 @@ typedef enum {
     KDA_BF16 = 1
 } kda_dtype;
 
+/* Layout of the decay gate g (kda_options.gate). */
+typedef enum {
+    KDA_GATE_CHANNEL = 0,   /* g [..][H][Dk]: one log-decay per key channel (KDA) */
+    KDA_GATE_HEAD = 1       /* g [..][H]: one per token and head (Gated DeltaNet);
+                               g NULL: no decay (DeltaNet) */
+} kda_gate;
+
+/*
+ * Options of kda_prefill_ex and kda_decode_ex. A zero-initialised struct (or
+ * a NULL pointer) gives kda_prefill's / kda_decode's behaviour.
+ *   gate           kda_gate value (else KDA_ERR_INVALID_ARG)
+ *   qk_l2norm      nonzero: q and k are L2-normalised over Dk inside the
+ *                  kernels, x <- x / sqrt(sum_c x_c^2 + l2norm_eps), as the
+ *                  explainer's KDA block does before the recurrence (its
+ *                  input-processing paragraph); the inputs are not modified
+ *   l2norm_eps     > 0 when qk_l2norm is set (else KDA_ERR_INVALID_ARG)
+ *   snapshot_every, max_snapshots, snapshots
+ *                  prefill only, as for kda_prefill_snapshots; snapshots NULL
+ *                  = none (decode: must be NULL)
+ */
+typedef struct {
+    int gate;
+    int qk_l2norm;
+    float l2norm_eps;
+    int snapshot_every;
+    int max_snapshots;
+    float *snapshots;
+} kda_options;
+
 /* Library version, (major << 16) | (minor << 8) | patch. */
 int kda_version(void);
 
@@ -187,6 +216,26 @@ int kda_decode(const void *q, const void *k, const void *v, const float *g,
 int gdn_decode(const void *q, const void *k, const void *v, const float *g,
                const void *beta, float *S, void *out, int N, int H, int Dk, int Dv,
                kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype, void *stream);
+
+/*
+ * kda_prefill_ex -- kda_prefill with options (gate layout, fused q/k L2
+ * normalisation, snapshots). The g layout follows opt->gate (see gdn_prefill
+ * for KDA_GATE_HEAD); everything else as kda_prefill, with the same workspace.
+ */
+int kda_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                   const void *beta, const float *S0, void *out, float *S_out,
+                   const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                   int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
+                   const kda_options *opt, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_ex -- kda_decode with options (gate layout as for gdn_decode
+ * when KDA_GATE_HEAD, fused q/k L2 normalisation; no snapshots).
+ */
+int kda_decode_ex(const void *q, const void *k, const void *v, const float *g,
+                  const void *beta, float *S, void *out, int N, int H, int Dk, int Dv,
+                  kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
+                  const kda_options *opt, void *stream);
 
 #ifdef __cplusplus
 }

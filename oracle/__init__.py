@@ -12,6 +12,9 @@ Two independent implementations live here:
 * ``chunked_naive.chunked``: the chunked (FlashKDA-style) matrix form in
   numpy, written separately, used only to cross-check the recurrence.
 
+``l2norm`` is the q/k pre-normalisation of the KDA block (explainer, input
+processing paragraph: L2 norm on q and k), written out as its definition.
+
 Both follow the Kimi K3 explainer (SemiAnalysis, Chinese translation):
 DeltaNet section (delta rule), GDN/KDA paragraph (per-channel diagonal
 forget gate) and FlashKDA paragraph (recurrence with D_t and u_t, chunk
@@ -134,3 +137,11 @@ def decode_step(q, k, v, g, beta, S, nthreads: Optional[int] = None):
     N = q.shape[0]
     cu = np.arange(N + 1, dtype=np.int64)
     return recurrent(q, k, v, g, beta, S0=S, cu_seqlens=cu, nthreads=nthreads)
+
+
+def l2norm(x, eps: float):
+    """x / sqrt(sum over the last axis of x^2 + eps), in fp64 (the L2 norm the
+    explainer's KDA block applies to q and k before the recurrence; eps as the
+    library takes it)."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)

@@ -168,3 +168,45 @@ def test_input_generators_are_deterministic():
     lens = inputs.varlen_lengths(16, 512, 16384, 1002)
     assert len(lens) == 16 and min(lens) >= 512 and max(lens) <= 16384
     assert lens == inputs.varlen_lengths(16, 512, 16384, 1002)
+
+
+def _opts(**kw):
+    from gated_delta_rule_103_amd.kda import Options
+    return ctypes.byref(Options(**kw))
+
+
+def _prefill_ex(lib, opt, **kw):
+    fake = ctypes.c_void_p(256)
+    a = dict(q=fake, k=fake, v=fake, g=fake, beta=fake, S0=None, out=fake, S_out=None,
+             cu=None, N=1, B=1, T=64, H=2, Dk=64, Dv=64, C=16, io=1, bd=1, od=1,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.kda_prefill_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["out"], a["S_out"],
+                              a["cu"], a["N"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["C"], a["io"],
+                              a["bd"], a["od"], opt, a["ws"], a["wsb"], a["stream"])
+
+
+# options are checked first; valid options fall through to kda_prefill's checks
+@pytest.mark.parametrize("opt,kw,status", [
+    (dict(gate=2), {}, -1), (dict(gate=-1), {}, -1),
+    (dict(qk_l2norm=1, l2norm_eps=0.0), {}, -1), (dict(qk_l2norm=1, l2norm_eps=-1.0), {}, -1),
+    (dict(qk_l2norm=1, l2norm_eps=float("nan")), {}, -1),
+    (dict(qk_l2norm=1, l2norm_eps=1e-6), dict(C=8), -2),
+    (dict(gate=1), dict(g=None, Dk=96, Dv=96), -2),          # per-head gate: NULL g allowed
+    (dict(gate=0), dict(g=None), -1),                        # per-channel gate: g required
+    (dict(snapshots=1 << 20, snapshot_every=16, max_snapshots=0), {}, -1),
+    (None, dict(q=None), -1),
+])
+def test_prefill_ex_argument_errors(lib, opt, kw, status):
+    assert _prefill_ex(lib, None if opt is None else _opts(**opt), **kw) == status
+
+
+def test_decode_ex_argument_errors(lib):
+    fake = ctypes.c_void_p(256)
+    call = lambda opt, **kw: lib.kda_decode_ex(fake, fake, fake, kw.get("g", fake), fake, fake, fake, 4, 2,
+                                               kw.get("D", 128), kw.get("D", 128), 1, 1, 1, opt, None)
+    assert call(_opts(snapshots=1 << 20)) == -1               # no snapshots in decode
+    assert call(_opts(qk_l2norm=1, l2norm_eps=0.0)) == -1
+    assert call(_opts(gate=3)) == -1
+    assert call(_opts(gate=1), g=None, D=32) == -2
+    assert call(None, D=32) == -2

@@ -338,3 +338,15 @@ def test_reference_mutant_is_faithful():
 def test_pins_catch_mutant(kind):
     failed = [pin.__name__ for pin, tol in PINS if not pin(_mutant(kind)) <= max(tol, 1e-12)]
     assert failed, f"no pin detects mutant {kind}"
+
+
+def test_l2norm_pins():
+    """oracle.l2norm against values fixed by its definition: a 3-4-5 triangle,
+    the eps term, scale invariance (eps = 0) and unit norms."""
+    np.testing.assert_allclose(oracle.l2norm([3.0, 4.0], 0.0), [0.6, 0.8], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(oracle.l2norm([3.0, 4.0], 11.0), [0.5, 2.0 / 3.0], rtol=0, atol=1e-15)
+    r = np.random.default_rng(5)
+    x = r.normal(size=(7, 3, 64))
+    np.testing.assert_allclose(oracle.l2norm(2.5 * x, 0.0), oracle.l2norm(x, 0.0), rtol=1e-14)
+    np.testing.assert_allclose(np.linalg.norm(oracle.l2norm(x, 0.0), axis=-1), 1.0, rtol=1e-14)
+    assert oracle.l2norm(x, 1e-6).shape == x.shape
