@@ -64,6 +64,9 @@ constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 #ifndef KDA_SPLIT_U
 #define KDA_SPLIT_U 1     // U in M += Kr^T U
 #endif
+#ifndef KDA_SCAN_BUFS
+#define KDA_SCAN_BUFS 3   // scan operand buffers in rotation: 3 = loads two chunks ahead, 2 = one chunk ahead
+#endif
 #ifndef KDA_SPLIT_UO
 #define KDA_SPLIT_UO 0    // U in O += Mqk U (o only)
 #endif
@@ -138,6 +141,7 @@ constexpr int SQ = D + 8;        // bf16 row stride of q, k           [64][136]
 constexpr int SE = D + 4;        // fp32 row stride of the decays     [64][132]
 constexpr int SL = C + 4;        // fp32 row stride of L / INV^T      [64][68]
 constexpr int SMQ = C + 8;       // fp16 row stride of Mqk            [64][72]
+constexpr int SKR = C + 8;       // fp16 row stride of Kr^T           [128][72]
 
 struct PrepLds {
     static constexpr int Q = 0;
@@ -150,13 +154,13 @@ struct PrepLds {
     static constexpr int BETA = DG + C * 4;          // fp32 [64]
     static constexpr int GB = BETA + C * 4;          // fp32 [4][128] block decays
     static constexpr int G = GB + 4 * D * 4;         // fp32 [4][128] decay chunk start -> block start
-    static constexpr int H = G + 4 * D * 4;          // fp32 [4][128] decay block end -> chunk end
-    static constexpr int GAM = H + 4 * D * 4;        // fp32 [128]
+    static constexpr int GAM = G + 4 * D * 4;        // fp32 [128]
     static constexpr int RQ = GAM + D * 4;           // fp32 [64] 1 / ||q_t|| (L2-normalised input)
     static constexpr int RK = RQ + C * 4;            // fp32 [64] 1 / ||k_t||
     static constexpr int FLAG = RK + C * 4;          // int [4]
     static constexpr int T3 = FLAG + 16;             // fp32 [3][256] inverse scratch
-    static constexpr int SIZE = T3 + 3 * 256 * 4;
+    static constexpr int KRT = T3 + 3 * 256 * 4;     // fp16 [128][SKR] Kr^T, channel-major
+    static constexpr int SIZE = KRT + D * SKR * 2;
 };
 
 struct PrepParams {
@@ -200,12 +204,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     float *sBeta = reinterpret_cast<float *>(smem + Lo::BETA);
     float *sGB = reinterpret_cast<float *>(smem + Lo::GB);
     float *sG = reinterpret_cast<float *>(smem + Lo::G);
-    float *sH = reinterpret_cast<float *>(smem + Lo::H);
     float *sGam = reinterpret_cast<float *>(smem + Lo::GAM);
     float *sRQ = reinterpret_cast<float *>(smem + Lo::RQ);
     float *sRK = reinterpret_cast<float *>(smem + Lo::RK);
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
     float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
+    _Float16 *sKrt = reinterpret_cast<_Float16 *>(smem + Lo::KRT);
 
     const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // 8 wavefronts
     const int H = p.H;
@@ -383,7 +387,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const int c = tid;
             const float g0 = sGB[c], g1 = sGB[D + c], g2 = sGB[2 * D + c], g3 = sGB[3 * D + c];
             sG[c] = 1.f; sG[D + c] = g0; sG[2 * D + c] = g0 * g1; sG[3 * D + c] = g0 * g1 * g2;
-            sH[3 * D + c] = 1.f; sH[2 * D + c] = g3; sH[D + c] = g2 * g3; sH[c] = g1 * g2 * g3;
             sGam[c] = g0 * g1 * g2 * g3;
         }
 
@@ -399,9 +402,11 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // once to fp16 (11-bit significand) and multiplied on fp16 MFMA. A wave's
         // blocks share their row block, so its left operands are built once.
         //   wavefront 4: (3,0) (3,1)   5: (3,2)   6: (2,0) (2,1)   7: (1,0)
+        // the four flags in one LDS read (a serial read per block cost a round trip each)
+        const int4 flags = *reinterpret_cast<const int4 *>(sFlag);
         if (wave < 4) {
             const int I = wave;
-            if (!sFlag[I]) {
+            if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) {
                 const int t = 16 * I + l16;
                 const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
                 f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
@@ -430,6 +435,42 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     // masked entries may hold inf / nan: select, do not scale
                     if (lower) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
                     sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
+                }
+            }
+            // Kr = k F H for the block's 16 tokens, written channel-major (Kr^T) so that
+            // the record's Kr^T fragments are single 16-byte reads. This wave is
+            // otherwise idle until the off-diagonal blocks are done. A lane takes a
+            // token pair (16I + 2(lane & 7), +1) and eight-channel groups lane >> 3 and
+            // (lane >> 3) + 8, and writes each (channel, token pair) as one dword.
+            {
+                const int t0 = 16 * I + 2 * (lane & 7);
+                float nk0 = 1.f, nk1 = 1.f;
+                if constexpr (NORM) { nk0 = sRK[t0]; nk1 = sRK[t0 + 1]; }
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int c0 = 8 * ((lane >> 3) + 8 * gg);
+                    // H (block I end -> chunk end) = product of the later block decays
+                    f32x4 h0 = {1.f, 1.f, 1.f, 1.f}, h1 = h0;
+#pragma unroll
+                    for (int K = 1; K < 4; ++K)
+                        if (K > I) {                                      // uniform
+                            h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
+                            h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
+                        }
+                    const bf16x8 ka = lds8(sK + t0 * SQ + c0), kb = lds8(sK + (t0 + 1) * SQ + c0);
+                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sF + t0 * SE + c0);
+                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sF + t0 * SE + c0 + 4);
+                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sF + (t0 + 1) * SE + c0);
+                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sF + (t0 + 1) * SE + c0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float hh = e < 4 ? h0[e] : h1[e - 4];
+                        const float xa = bf2f(ka[e]) * nk0 * (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
+                        const float xb = bf2f(kb[e]) * nk1 * (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
+                        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+                        const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
+                        *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
+                    }
                 }
             }
         } else {
@@ -491,8 +532,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         // exact path for diagonal blocks whose in-block decay leaves the fp32 normal range
-        for (int I = 0; I < 4; ++I) {
-            if (!sFlag[I]) continue;                     // uniform across the workgroup
+        for (int I = 0; I < 4 && (flags.x | flags.y | flags.z | flags.w); ++I) {
+            if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) continue;   // uniform
             if (wave == I) {
                 for (int tr = 1; tr < 16; ++tr)
                     for (int sc = 0; sc < tr; ++sc) {
@@ -525,18 +566,20 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         fetch(next, 2);
 
         // ================= INV = (I + L)^{-1}, stored transposed in the upper triangle
-        // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II
+        // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II, by
+        // column-oriented substitution: once x[sc] is final it is eliminated from
+        // every later row at once, so the updates of a step are independent and the
+        // L column reads (wave-uniform addresses) do not wait on the arithmetic.
+        // Entries above the diagonal stay 0 (they only ever see x[sc] = 0).
         if (wave < 4 && lane < 16) {
             const int I = wave, col = lane;
             float x[16];
 #pragma unroll
-            for (int tr = 0; tr < 16; ++tr) {
-                float v = (tr == col) ? 1.f : 0.f;
+            for (int tr = 0; tr < 16; ++tr) x[tr] = (tr == col) ? 1.f : 0.f;
 #pragma unroll
-                for (int sc = 0; sc < tr; ++sc) v -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
-                x[tr] = (tr < col) ? 0.f : v;
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int sc = 0; sc < 15; ++sc)
+#pragma unroll
+                for (int tr = sc + 1; tr < 16; ++tr) x[tr] -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
 #pragma unroll
             for (int tr = 0; tr < 16; ++tr)
                 if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
@@ -607,27 +650,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     }
                 }
             } else {
+                // Kr^T fragments (channel rows, tokens 32ks + 8lq .. +7), built by waves 0-3
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const int chn = 32 * role + 16 * rt + l16;
+                for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        // tokens 32ks + 8lq .. +7 lie in one 16-token block
-                        const float hb = sH[(2 * ks + (lq >> 1)) * D + chn];
-                        f32x4 n0 = {1.f, 1.f, 1.f, 1.f}, n1 = n0;
-                        if constexpr (NORM) {
-                            n0 = *reinterpret_cast<const f32x4 *>(sRK + 32 * ks + 8 * lq);
-                            n1 = *reinterpret_cast<const f32x4 *>(sRK + 32 * ks + 8 * lq + 4);
-                        }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int tt = 32 * ks + 8 * lq + e;
-                            const float kk = NORM ? bf2f(sK[tt * SQ + chn]) * (e < 4 ? n0[e] : n1[e - 4])
-                                                  : bf2f(sK[tt * SQ + chn]);
-                            fr[rt * 2 + ks][e] = static_cast<_Float16>(kk * sF[tt * SE + chn] * hb);
-                        }
-                    }
-                }
+                    for (int ks = 0; ks < 2; ++ks)
+                        fr[rt * 2 + ks] = lds8h(sKrt + (32 * role + 16 * rt + l16) * SKR + 32 * ks + 8 * lq);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const f32x4 be0 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq);
@@ -923,6 +951,7 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
     // The prefetches are unconditional (the chunk index is clamped, so the tail
     // re-reads the last record): conditional loads would make every later wait
     // on vector memory conservative and defeat the prefetch.
+#if KDA_SCAN_BUFS == 3
     Frags A, B, Cb;
     if (nch > 0) {
         const int last = nch - 1;
@@ -936,6 +965,19 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
             step(Cb, j + 2, B, min(j + 4, last));
         }
     }
+#else
+    // two operand buffers: a chunk's loads are issued during the step before it
+    Frags A, B;
+    if (nch > 0) {
+        const int last = nch - 1;
+        issue(0, A, 0, NLD);
+        for (int j = 0; j < nch; j += 2) {
+            step(A, j, B, min(j + 1, last));
+            if (j + 1 >= nch) break;
+            step(B, j + 1, A, min(j + 2, last));
+        }
+    }
+#endif
 
     if (p.S_out) {
 #pragma unroll
