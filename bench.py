@@ -22,7 +22,7 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from gated_delta_rule_103_amd import costs, inputs, kda_decode, kda_prefill  # noqa: E402
+from gated_delta_rule_103_amd import costs, inputs, kda_decode, kda_output_gate, kda_prefill  # noqa: E402
 from gated_delta_rule_103_amd.kda import kda_prefill_workspace_size  # noqa: E402
 
 PREFILL_WORKLOAD = "single_seq_8k"
@@ -95,6 +95,21 @@ def bench_decode(steps, warmup):
                 frac_hbm=state_bytes / (ms_step * 1e-3) / 1e9 / costs.MI355X_PEAK["hbm_GBps"])
 
 
+def bench_output_gate(steps, warmup, shape):
+    """kda_output_gate over a prefill output of `shape` (rows, H, Dv): bf16 o and
+    gate, fp32 weight, bf16 out. Bound by HBM: o and gate read once, out written once."""
+    rows, H, Dv = shape
+    x = inputs.output_gate(rows, H, Dv, o_io="bf16", gate_io="bf16", o_std=0.3, seed=1001, device="cuda")
+    out = torch.empty_like(x.o)
+
+    def step():
+        kda_output_gate(x.o, x.gate, x.weight, out=out)
+
+    _, ms = _time_region(step, steps, warmup)
+    nbytes = rows * H * Dv * 3 * 2 + Dv * 4
+    return dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9)
+
+
 def cpu_baseline(p, min_seconds=10.0):
     """The fp64 oracle on the whole single-sequence workload (32 heads x 8192
     tokens), repeated until about `min_seconds` of host time has been spent."""
@@ -164,6 +179,8 @@ def main():
     gbps = pf["min_bytes"] / k_s / 1e9
     value = pf["tokens"] * args.steps / pf["wall_s"] / 1e6
     dec = None if args.no_decode else bench_decode(max(1, args.steps // 4), 1)
+    og = bench_output_gate(args.steps, args.warmup, (pf["tokens"], w_h := inputs.WORKLOADS[args.workload]["H"],
+                                                     inputs.WORKLOADS[args.workload]["D"]))
     cpu = None if (args.no_cpu_baseline or args.workload != PREFILL_WORKLOAD) else cpu_baseline(pf["inputs"])
 
     w = inputs.WORKLOADS[args.workload]
@@ -202,6 +219,10 @@ def main():
                                        "traffic": measured_traffic("kda_decode", DECODE_WORKLOAD),
                                        "model": "8*D^2 bytes per head-step"},
                           "gbps_incl_vectors": round(dec["gbps_total"], 1)}
+    line["output_gate"] = {"shape": [pf["tokens"], w_h, w["D"]], "ms_per_call": round(og["ms"], 4),
+                           "roofline": {"bound": "hbm", "achieved": round(og["gbps"], 1), "peak": peak_bw,
+                                        "unit": "GB/s", "frac": round(og["gbps"] / peak_bw, 4),
+                                        "model": "read o and gate, write out (bf16), once each"}}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -210,3 +210,29 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int kda_output_gate(const void *o, const void *gate, const float *weight, void *out, int rows, int H, int Dv,
+                    float eps, kda_dtype o_dtype, kda_dtype gate_dtype, kda_dtype out_dtype, void *stream) {
+    if (rows < 0 || H < 1 || Dv < 1 || !(eps > 0.f)) return KDA_ERR_INVALID_ARG;     // also rejects NaN eps
+    if (rows > 0 && (!o || !gate || !out)) return KDA_ERR_INVALID_ARG;          // empty tensors may be NULL
+    if (!dtype_ok(o_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_INVALID_ARG;
+    if ((long long)rows * H > INT_MAX) return KDA_ERR_INVALID_ARG;
+    // eight channels per lane: 16-byte vector loads and stores
+    if ((reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(gate) | reinterpret_cast<uintptr_t>(out) |
+         reinterpret_cast<uintptr_t>(weight)) & 15u)
+        return KDA_ERR_INVALID_ARG;
+    // in place only with the same element type (each lane rewrites what it read)
+    if (rows > 0 && out == o && out_dtype != o_dtype) return KDA_ERR_INVALID_ARG;
+    if (Dv != 64 && Dv != 128) return KDA_ERR_UNSUPPORTED;
+    kda::OutputGateArgs a;
+    a.o = o; a.gate = gate; a.weight = weight; a.out = out;
+    a.rows = rows; a.H = H; a.Dv = Dv; a.eps = eps;
+    a.o_dt = static_cast<Dt>(o_dtype); a.gate_dt = static_cast<Dt>(gate_dtype);
+    a.out_dt = static_cast<Dt>(out_dtype);
+    a.stream = static_cast<hipStream_t>(stream);
+    return kda::launch_output_gate(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -50,6 +50,16 @@ struct DecodeArgs {
     float norm_eps = 0.f;
 };
 
+struct OutputGateArgs {
+    const void *o, *gate;
+    const float *weight;        // [Dv] or nullptr (ones)
+    void *out;
+    int rows, H, Dv;
+    float eps;
+    Dt o_dt, gate_dt, out_dt;
+    hipStream_t stream;
+};
+
 // Upper bound on the number of chunks of all sequences (each sequence adds at
 // most one partial chunk).
 inline long long max_chunks(int N, long long T_total, int C) {
@@ -69,5 +79,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a);
 
 // single-token decode.
 hipError_t launch_decode(const DecodeArgs &a);
+
+// per-head RMS norm and sigmoid output gate of o.
+hipError_t launch_output_gate(const OutputGateArgs &a);
 
 }  // namespace kda

@@ -193,3 +193,23 @@ def workload_decode(name: str = "decode_512x32", device="cpu") -> DecodeInputs:
     w = WORKLOADS[name]
     return decode(w["N"], w["H"], w["D"], w["steps"], io=w["io"], shift=w["shift"],
                   state_std=w["state_std"], seed=w["seed"], device=device)
+
+
+@dataclass
+class OutputGateInputs:
+    o: torch.Tensor            # [rows, H, Dv] o dtype
+    gate: torch.Tensor         # [rows, H, Dv] gate dtype (pre-activation)
+    weight: Optional[torch.Tensor]   # [Dv] fp32 or None
+
+
+def output_gate(rows: int, H: int, Dv: int, *, o_io: str = "bf16", gate_io: str = "bf16",
+                o_std: float = 1.0, with_weight: bool = True, seed: int = 0,
+                device="cpu") -> OutputGateInputs:
+    """Inputs of the output norm and gate: o ~ N(0, o_std^2) (an attention output),
+    gate pre-activation ~ N(0, 2^2), weight ~ N(1, 0.1^2) fp32. Draw order: o, gate,
+    weight."""
+    gen = _gen(seed, device)
+    o = (torch.randn(rows, H, Dv, generator=gen, device=device) * o_std).to(_DT[o_io])
+    gate = (torch.randn(rows, H, Dv, generator=gen, device=device) * 2.0).to(_DT[gate_io])
+    w = 1.0 + 0.1 * torch.randn(Dv, generator=gen, device=device)
+    return OutputGateInputs(o=o, gate=gate, weight=w if with_weight else None)

@@ -75,6 +75,8 @@ def load_library() -> ctypes.CDLL:
                                    i, i, i, i, i, i, i, i, i, i, op, vp, sz, vp]
     lib.kda_decode_ex.restype = i
     lib.kda_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, op, vp]
+    lib.kda_output_gate.restype = i
+    lib.kda_output_gate.argtypes = [vp, vp, vp, vp, i, i, i, ctypes.c_float, i, i, i, vp]
     _lib = lib
     return lib
 
@@ -214,3 +216,25 @@ def gdn_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype
     """kda_decode with the scalar gate of Gated DeltaNet: g [N, H] fp32, or None
     for DeltaNet (no decay)."""
     return _decode("gdn_decode", q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm, l2norm_eps)
+
+
+def kda_output_gate(o, gate, weight=None, *, eps: float = 1e-6, out=None,
+                    out_dtype: Optional[torch.dtype] = None, stream=None):
+    """Per-head RMS norm of o with a per-channel weight and a sigmoid output gate:
+    out = o / sqrt(mean(o^2 over Dv) + eps) * weight * sigmoid(gate).
+    o, gate: [..., H, Dv] (same shape); weight: [Dv] fp32 or None (ones).
+    ``out`` may be ``o`` itself when the dtypes match. Returns out."""
+    lib = load_library()
+    if gate.shape != o.shape:
+        raise ValueError("gate must have the shape of o")
+    H, Dv = o.shape[-2], o.shape[-1]
+    rows = o.numel() // (H * Dv) if o.numel() else 0
+    if weight is not None and (weight.dtype != torch.float32 or weight.numel() != Dv):
+        raise ValueError("weight must be a float32 tensor of Dv elements")
+    if out is None:
+        out = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=o.device)
+    st = lib.kda_output_gate(_ptr(o), _ptr(gate), _ptr(weight), _ptr(out), rows, H, Dv, float(eps),
+                             _dt(o), _dt(gate), _dt(out), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_output_gate")
+    return out

@@ -237,6 +237,34 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g,
                   kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
                   const kda_options *opt, void *stream);
 
+/*
+ * kda_output_gate -- the output side of the KDA block: per-head RMS norm of
+ * the attention output, a per-channel weight and a sigmoid output gate. The
+ * explainer's KDA section (its input/output paragraph) says KDA's output is
+ * normalised per head and controlled by an output forget gate computed by a
+ * projection; the projection needs trained weights, so the caller passes its
+ * result (the gate pre-activation z). Per row r, head h and channel j:
+ *     out[r][h][j] = o[r][h][j] / sqrt(mean_j' o[r][h][j']^2 + eps)
+ *                    * weight[j] * 1 / (1 + exp(-z[r][h][j]))
+ *   o        [rows][H][Dv] o_dtype (e.g. kda_prefill's out, rows = tokens, or
+ *            kda_decode's out, rows = sequences)
+ *   gate     [rows][H][Dv] gate_dtype, the pre-activation z
+ *   weight   [Dv] fp32, shared by the heads; NULL = all ones
+ *   out      [rows][H][Dv] out_dtype; may be o itself when out_dtype ==
+ *            o_dtype (in place), no other overlap is allowed
+ *   eps      > 0
+ * o, gate, out and weight must be 16-byte aligned. Supported: Dv in {64, 128}
+ * (else KDA_ERR_UNSUPPORTED); rows == 0 launches nothing (o, gate and out may
+ * then be NULL). Arithmetic in fp32; a bf16 out is the round-to-nearest-even
+ * of the fp32 result. Errors:
+ * KDA_ERR_INVALID_ARG for NULL o / gate / out with rows > 0, rows < 0, H < 1, Dv < 1,
+ * eps <= 0 or NaN, a bad dtype, misalignment, rows * H > INT_MAX, or an
+ * in-place call that changes the dtype.
+ */
+int kda_output_gate(const void *o, const void *gate, const float *weight, void *out, int rows, int H,
+                    int Dv, float eps, kda_dtype o_dtype, kda_dtype gate_dtype, kda_dtype out_dtype,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -210,3 +210,29 @@ def test_decode_ex_argument_errors(lib):
     assert call(_opts(gate=3)) == -1
     assert call(_opts(gate=1), g=None, D=32) == -2
     assert call(None, D=32) == -2
+
+
+def _output_gate(lib, **kw):
+    fake = ctypes.c_void_p(256)          # never dereferenced: checks return first
+    a = dict(o=fake, gate=fake, w=None, out=ctypes.c_void_p(4096), rows=4, H=2, Dv=64, eps=1e-6,
+             od=1, gd=1, outd=1, stream=None)
+    a.update(kw)
+    return lib.kda_output_gate(a["o"], a["gate"], a["w"], a["out"], a["rows"], a["H"], a["Dv"],
+                               a["eps"], a["od"], a["gd"], a["outd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), -1), (dict(gate=None), -1), (dict(out=None), -1),
+    (dict(rows=-1), -1), (dict(H=0), -1), (dict(Dv=0), -1),
+    (dict(eps=0.0), -1), (dict(eps=-1.0), -1), (dict(eps=float("nan")), -1),
+    (dict(od=2), -1), (dict(gd=5), -1), (dict(outd=-1), -1),
+    (dict(o=ctypes.c_void_p(264)), -1), (dict(w=ctypes.c_void_p(260)), -1),
+    (dict(out=ctypes.c_void_p(256), outd=0), -1),            # in place with a dtype change
+    (dict(rows=1 << 20, H=4096), -1),
+    (dict(Dv=96), -2), (dict(Dv=256), -2),
+    (dict(rows=0), 0),                                        # nothing to do, nothing launched
+    (dict(rows=0, o=None, gate=None, out=None), 0),           # empty tensors may be NULL
+    (dict(rows=0, o=None, gate=None, out=None, outd=0), 0),
+])
+def test_output_gate_argument_errors(lib, kw, status):
+    assert _output_gate(lib, **kw) == status

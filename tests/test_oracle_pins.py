@@ -350,3 +350,63 @@ def test_l2norm_pins():
     np.testing.assert_allclose(oracle.l2norm(2.5 * x, 0.0), oracle.l2norm(x, 0.0), rtol=1e-14)
     np.testing.assert_allclose(np.linalg.norm(oracle.l2norm(x, 0.0), axis=-1), 1.0, rtol=1e-14)
     assert oracle.l2norm(x, 1e-6).shape == x.shape
+
+
+# ---------------------------------------------------------------- output norm and gate
+OUTPUT_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "output_gate_hand.json")
+
+
+def _output_gate_mutants():
+    """Plausible mistakes in the output side, each of which a pin below must reject."""
+    def sum_not_mean(o, gate, weight=None, eps=1e-6):
+        o = np.asarray(o, float)
+        return o / np.sqrt(np.sum(o * o, -1, keepdims=True) + eps) * (1 if weight is None else weight) / (1 + np.exp(-np.asarray(gate)))
+
+    def eps_outside(o, gate, weight=None, eps=1e-6):
+        o = np.asarray(o, float)
+        return o / (np.sqrt(np.mean(o * o, -1, keepdims=True)) + eps) * (1 if weight is None else weight) / (1 + np.exp(-np.asarray(gate)))
+
+    def gate_sign(o, gate, weight=None, eps=1e-6):
+        o = np.asarray(o, float)
+        return o / np.sqrt(np.mean(o * o, -1, keepdims=True) + eps) * (1 if weight is None else weight) / (1 + np.exp(np.asarray(gate)))
+
+    def norm_over_heads(o, gate, weight=None, eps=1e-6):
+        o = np.asarray(o, float)
+        return o / np.sqrt(np.mean(o * o, axis=(-2, -1), keepdims=True) + eps) * (1 if weight is None else weight) / (1 + np.exp(-np.asarray(gate)))
+    return dict(sum_not_mean=sum_not_mean, eps_outside=eps_outside, gate_sign=gate_sign,
+                norm_over_heads=norm_over_heads)
+
+
+def _output_gate_pins(fn):
+    """True when fn satisfies every output-side pin: the hand-worked cases, and the
+    invariants an RMS norm with a sigmoid gate must have."""
+    ok = True
+    for c in json.load(open(OUTPUT_GOLDEN))["cases"]:
+        w = None if c["weight"] is None else np.array(c["weight"])
+        got = fn(np.array(c["o"]), np.array(c["gate"]), w, eps=c["eps"])
+        ok &= np.allclose(got, np.array(c["out"]), rtol=1e-14, atol=1e-15)
+    rng = np.random.default_rng(7)
+    o = rng.normal(size=(5, 3, 16))
+    z = rng.normal(size=(5, 3, 16))
+    base = fn(o, z, None, eps=0.0)
+    # scale invariance of the norm (eps = 0) and oddness in o
+    ok &= np.allclose(fn(7.5 * o, z, None, eps=0.0), base, rtol=1e-13)
+    ok &= np.allclose(fn(-o, z, None, eps=0.0), -base, rtol=1e-13)
+    # an open gate (z -> +inf) leaves unit RMS per head; a closed one gives 0
+    opened = fn(o, np.full_like(z, 60.0), None, eps=0.0)
+    ok &= np.allclose(np.sqrt(np.mean(opened ** 2, -1)), 1.0, rtol=1e-12)
+    ok &= np.allclose(fn(o, np.full_like(z, -60.0), None, eps=0.0), 0.0, atol=1e-20)
+    # with eps the RMS becomes sqrt(ms / (ms + eps))
+    ms = np.mean(o * o, -1)
+    ok &= np.allclose(np.sqrt(np.mean(fn(o, np.full_like(z, 60.0), None, eps=0.5) ** 2, -1)),
+                      np.sqrt(ms / (ms + 0.5)), rtol=1e-12)
+    return bool(ok)
+
+
+def test_output_gate_pins():
+    assert _output_gate_pins(oracle.output_gate)
+
+
+@pytest.mark.parametrize("kind", sorted(_output_gate_mutants()))
+def test_output_gate_pins_catch_mutant(kind):
+    assert not _output_gate_pins(_output_gate_mutants()[kind])
