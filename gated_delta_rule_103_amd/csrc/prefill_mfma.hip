@@ -233,7 +233,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     if constexpr (VARLEN)
         if ((int)blockIdx.x < items) meta_ahead = p.meta[(int)blockIdx.x / H];
     u32x4 rq[2], rk[2];
-    f32x4 rg[4];
+    float rg[16];                // g of (token 16 (tid >> 7) + tt, channel tid & 127), tt < 16
     TB rbeta = TB(0);
     int nx_h = 0, nx_tok0 = 0, nx_Lc = 0;
     // part 0: chunk bounds, q and k; part 1: g; part 2: beta; -1: all. The
@@ -264,22 +264,22 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         if (part == -1 || part == 1) {
+            // thread (block I, channel c) takes the 16 rows of its block at its
+            // channel: for each row the 128 threads of a block read 512
+            // contiguous bytes, and the decay products then stay in registers
+            const int I = tid0 >> 7, c = tid0 & (D - 1);
             if constexpr (GHEAD) {
                 // one value per row, broadcast over the channels; without a gate the
                 // range is empty and every load reads 0 (alpha = 1)
                 const auto rgh = buf_rsrc(p.g ? p.g + (size_t)tok0 * H + h : nullptr, p.g ? ((Lc - 1) * H + 1) * 4 : 0);
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int row = (tid0 + it * PTHR) >> 5;
-                    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgh, min(row, Lc - 1) * H * 4, 0, 0));
-                    rg[it] = f32x4{x, x, x, x};
-                }
+                for (int tt = 0; tt < 16; ++tt)
+                    rg[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgh, min(16 * I + tt, Lc - 1) * H * 4, 0, 0));
             } else {
+                const auto rgc = buf_rsrc(p.g + ((size_t)tok0 * H + h) * D, ((Lc - 1) * H + 1) * D * 4);
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int idx = tid0 + it * PTHR, row = idx >> 5, part = idx & 31;
-                    rg[it] = *reinterpret_cast<const f32x4 *>(p.g + ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 4 * part);
-                }
+                for (int tt = 0; tt < 16; ++tt)
+                    rg[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgc, (min(16 * I + tt, Lc - 1) * H * D + c) * 4, 0, 0));
             }
         }
         if (part == -1 || part == 2)
@@ -324,27 +324,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 }
             }
         }
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid + it * PTHR, row = idx >> 5, part = idx & 31;
-            f32x4 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = row < Lc ? __expf(rg[it][e]) : 1.f;
-            *reinterpret_cast<f32x4 *>(sE + row * SE + 4 * part) = a;
-        }
-        if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
-        if (tid < 4) sFlag[tid] = 0;
-        __syncthreads();
-        // the next item's inputs, in flight while this one is computed
-        const int next = min(item + (int)gridDim.x, items - 1);
-        fetch(next, 0);
-
-        // ================= in-block suffix (F) and prefix (E) products of alpha
+        // in-block suffix (F) and prefix (E) products of alpha = exp(g), one
+        // (block, channel) per thread, from the registers (rows past the end: alpha = 1)
         {
-            const int I = tid >> 7, c = tid & 127;          // one (block, channel) per thread
+            const int I = tid >> 7, c = tid & 127;
             float al[16];
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) al[tt] = sE[(16 * I + tt) * SE + c];
+            for (int tt = 0; tt < 16; ++tt) al[tt] = 16 * I + tt < Lc ? __expf(rg[tt]) : 1.f;
             float f = 1.f;
 #pragma unroll
             for (int tt = 15; tt >= 0; --tt) {
@@ -358,31 +344,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 sE[(16 * I + tt) * SE + c] = e;
             }
             sGB[I * D + c] = e;
-            if (!(e >= kTiny)) atomicOr(&sFlag[I], 1);
+            if (!(e >= kTiny)) atomicOr(&sFlag[I], 1);     // flags were cleared during the previous item
         }
-        // exact diagonal d_t = q_t . k_t (8 lanes per row, 16 channels each)
-        {
-            const int row = tid >> 3, seg = tid & 7;
-            const bf16x8 qa = lds8(sQ + row * SQ + 16 * seg), qb = lds8(sQ + row * SQ + 16 * seg + 8);
-            const bf16x8 ka = lds8(sK + row * SQ + 16 * seg), kb = lds8(sK + row * SQ + 16 * seg + 8);
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc += bf2f(qa[e]) * bf2f(ka[e]) + bf2f(qb[e]) * bf2f(kb[e]);
-            acc += __shfl_xor(acc, 1, 64);
-            acc += __shfl_xor(acc, 2, 64);
-            acc += __shfl_xor(acc, 4, 64);
-            if constexpr (NORM) acc *= sRQ[row] * sRK[row];
-            if (seg == 0) sDg[row] = acc;
-        }
-        // zero the upper blocks of Mqk (never written below)
-        for (int idx = tid; idx < 6 * 256; idx += PTHR) {
-            const int bb = idx >> 8, e = idx & 255;
-            int I, J;
-            if (bb < 3) { I = bb; J = bb + 1; } else if (bb < 5) { I = bb - 3; J = I + 2; } else { I = 0; J = 3; }
-            sMqk[(16 * I + (e >> 4)) * SMQ + 16 * J + (e & 15)] = static_cast<_Float16>(0.f);
-        }
+        if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
         __syncthreads();
-        fetch(next, 1);
+        // the next item's inputs, in flight while this one is computed
+        const int next = min(item + (int)gridDim.x, items - 1);
+        fetch(next, 0);
         if (tid < D) {
             const int c = tid;
             const float g0 = sGB[c], g1 = sGB[D + c], g2 = sGB[2 * D + c], g3 = sGB[3 * D + c];
@@ -472,6 +440,28 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
                     }
                 }
+            }
+            // exact diagonal d_t = q_t . k_t (4 lanes per row, 32 channels each)
+            {
+                const int row = tid >> 2, seg = tid & 3;
+                float acc = 0.f;
+#pragma unroll
+                for (int hh = 0; hh < 4; ++hh) {
+                    const bf16x8 qa = lds8(sQ + row * SQ + 32 * seg + 8 * hh), ka = lds8(sK + row * SQ + 32 * seg + 8 * hh);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc += bf2f(qa[e]) * bf2f(ka[e]);
+                }
+                acc += __shfl_xor(acc, 1, 64);
+                acc += __shfl_xor(acc, 2, 64);
+                if constexpr (NORM) acc *= sRQ[row] * sRK[row];
+                if (seg == 0) sDg[row] = acc;
+            }
+            // zero the upper blocks of Mqk (never written elsewhere)
+            for (int idx = tid; idx < 6 * 256; idx += 256) {
+                const int bb = idx >> 8, e = idx & 255;
+                int I2, J2;
+                if (bb < 3) { I2 = bb; J2 = bb + 1; } else if (bb < 5) { I2 = bb - 3; J2 = I2 + 2; } else { I2 = 0; J2 = 3; }
+                sMqk[(16 * I2 + (e >> 4)) * SMQ + 16 * J2 + (e & 15)] = static_cast<_Float16>(0.f);
             }
         } else {
             const int I = wave == 6 ? 2 : wave == 7 ? 1 : 3;
@@ -563,7 +553,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         __syncthreads();
-        fetch(next, 2);
+        fetch(next, 1);
+        // the flags were read above (into registers); clear them for the next item
+        if (tid < 4) sFlag[tid] = 0;
 
         // ================= INV = (I + L)^{-1}, stored transposed in the upper triangle
         // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II, by
@@ -585,6 +577,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
         }
         __syncthreads();
+        fetch(next, 2);
         // off-diagonal blocks, one level (I - J) at a time, on fp32 MFMA (exact products):
         //   T = sum_{K=J}^{I-1} L_IK INV_KJ ;  INV_IJ = -INV_II T
         // INV_XY[a][b] lives at sLI[(16Y + b) * SL + 16X + a]; for X == Y only a >= b is stored.
@@ -689,6 +682,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         }
         __syncthreads();      // LDS is restaged by the next item
     };
+    if (tid0 < 4) sFlag[tid0] = 0;
+    __syncthreads();
     if ((int)blockIdx.x < items) {
         fetch(blockIdx.x, -1);
         body(blockIdx.x);
