@@ -73,9 +73,10 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     if (cu_seqlens ? B != 1 : N != B) return KDA_ERR_INVALID_ARG;
     const long long T_total = (long long)B * T;
     if (T_total > INT_MAX / 2 || (long long)N * H > INT_MAX / 2) return KDA_ERR_INVALID_ARG;
-    // q, k, v and a per-channel g are read with 16-byte vector loads
+    // q, k, v and a per-channel g are read with 16-byte vector loads; out is
+    // written with vector stores of up to 16 bytes
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
-         (g_head ? 0u : reinterpret_cast<uintptr_t>(g))) & 15u)
+         reinterpret_cast<uintptr_t>(out) | (g_head ? 0u : reinterpret_cast<uintptr_t>(g))) & 15u)
         return KDA_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(g) & 3u) return KDA_ERR_INVALID_ARG;
     if (snapshots) {

@@ -65,7 +65,7 @@ constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 #define KDA_SPLIT_U 1     // U in M += Kr^T U
 #endif
 #ifndef KDA_SCAN_BUFS
-#define KDA_SCAN_BUFS 3   // scan operand buffers in rotation: 3 = loads two chunks ahead, 2 = one chunk ahead
+#define KDA_SCAN_BUFS 3   // scan operand buffers in rotation (loads two chunks ahead)
 #endif
 #ifndef KDA_SPLIT_UO
 #define KDA_SPLIT_UO 0    // U in O += Mqk U (o only)
@@ -694,13 +694,17 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 // ---------------------------------------------------------------- scan
 constexpr int SMS = D + 8;       // fp16 row stride of the state       [col][136]
 constexpr int SYU = C + 8;       // fp16 row stride of Y and U         [col][72]
+constexpr int SVT = C + 8;       // bf16 row stride of the V tile      [col][72]
 
 template <int TV>
 struct ScanLds {
     static constexpr int M = 0;                      // fp16 [2][TV][SMS] state hi / lo, [col][channel]
     static constexpr int Y = M + 2 * TV * SMS * 2;   // fp16 [2][TV][SYU] (V - Kd M) hi / lo, [col][token]
     static constexpr int U = Y + 2 * TV * SYU * 2;   // fp16 [2][TV][SYU] U hi / lo, [col][token]
-    static constexpr int SIZE = U + 2 * TV * SYU * 2;
+    static constexpr int V = U + 2 * TV * SYU * 2;   // bf16 [2][TV][SVT] V of a chunk, [col][token], double-buffered
+    static constexpr int DG = V + 2 * TV * SVT * 2;  // fp32 [2][C + D] d then gamma of a chunk, double-buffered
+    static constexpr int UF = DG + 2 * (C + D) * 4;  // fp32 [C][TV] U, [token][col]
+    static constexpr int SIZE = UF + C * TV * 4;
 };
 
 struct ScanParams {
@@ -715,20 +719,37 @@ struct ScanParams {
     SnapView snap;
 };
 
+template <typename T> __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x);
+template <> __device__ __forceinline__ void buf_st4<float>(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, 0, 0);
+}
+template <> __device__ __forceinline__ void buf_st4<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[0])) |
+                        (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[1]))) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2])) |
+                        (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[3]))) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, voff, 0, 0);
+}
+
 template <int TV, typename TO>
 __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = ScanLds<TV>;
     constexpr int NT = TV / 16;
     constexpr int TEAM = D / TV;
+    static_assert(NT == 1, "one 16-column tile per workgroup: the V tile is staged by 128 lanes of 16 bytes");
     _Float16 *sMh = reinterpret_cast<_Float16 *>(smem + Lo::M);
     _Float16 *sMl = sMh + TV * SMS;
     _Float16 *sYh = reinterpret_cast<_Float16 *>(smem + Lo::Y);
     _Float16 *sYl = sYh + TV * SYU;
     _Float16 *sUh = reinterpret_cast<_Float16 *>(smem + Lo::U);
     _Float16 *sUl = sUh + TV * SYU;
+    bf16_t *sV = reinterpret_cast<bf16_t *>(smem + Lo::V);
+    float *sDG = reinterpret_cast<float *>(smem + Lo::DG);
+    float *sUf = reinterpret_cast<float *>(smem + Lo::UF);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     // XCD-aware placement: block b runs on XCD b % 8; the TEAM workgroups of
     // one chain share b % 8 and so one L2, where the chain's records are read.
@@ -769,36 +790,36 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
             }
     };
     publish_state();
-    __syncthreads();
 
-    // operands of one chunk, loaded one chunk ahead
+    // operands of one chunk, loaded two chunks ahead
     struct Frags {
         f16x8 kd[4], qd[4], ib[2], mq[2], kr[2][2];
-        f32x4 dg, gam[2];
-        uint32_t v[NT][4];        // bf16 bits of V (tokens tb + 4lq + i, column l16 of tile nt)
+        // one 16-byte piece of the chunk's V tile (waves 0-1: token (tid >> 1),
+        // columns 8 (tid & 1) .. +7) or of its d and gamma, which are adjacent in
+        // the record (waves 2-3: floats 4 (tid - 128) .. +3 of the 192; lanes past
+        // them repeat the last piece), staged through LDS one chunk ahead
+        u32x4 x;
     };
-    // loop-invariant byte offsets of this lane's record fragments, and of its
-    // (token tb + 4lq + i, column col0 + 16nt + l16) elements from a chunk's
-    // first row in v (bf16) and in out
+    // loop-invariant byte offsets of this lane's record fragments
     const int r_frag = wave * Rec::WAVE + lane * 16;
-    const int r_dg = (tb + 4 * lq) * 4, r_gam = (32 * wave + 4 * lq) * 4;
-    int v_off[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v_off[nt][i] = ((tb + 4 * lq + i) * H * D + col0 + 16 * nt + l16) * 2;
+    const bool x_is_v = wave < 2;                                  // uniform
+    static_assert(Rec::GAM == Rec::DG + C * 4, "d and gamma adjacent in the record");
+    const int x_off = x_is_v ? ((tid >> 1) * H * D + col0 + 8 * (tid & 1)) * 2
+                             : Rec::DG + 16 * min(tid - 128, (C + D) / 4 - 1);
+    // this lane's output: token tb + l16, columns col0 + 4lq .. +3 (O is formed transposed)
+    const int o_off = ((tb + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
     // bytes from a chunk's first row to the end of its last valid row
     auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
 
     // The loads of one chunk's operands, as NLD slots in the order they are
-    // consumed: Kd and Qd by k-step, V, IB, gamma, Kr, Mqk, d. issue() sends
-    // slots [s0, s1); the step spreads them over its phases, so that no wave
-    // stalls on a full vector-memory queue with work of its own waiting.
-    constexpr int NLD = 19 + 4 * NT;
+    // consumed: Kd and Qd by k-step, the V / gamma piece, IB, Kr, Mqk. issue()
+    // sends slots [s0, s1); the step spreads them over its phases, so that no
+    // wave stalls on a full vector-memory queue with work of its own waiting.
+    constexpr int NLD = 17;
     auto issue = [&](int j, Frags &f, int s0, int s1) {
         const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
         const int tok0 = start + j * C, Lc = min(C, end - tok0);
-        // rows past the end of the sequence read 0 (outside the range): their values
+        // V rows past the end of the sequence read 0 (outside the range): their values
         // never matter, because beta = 0 there makes the matching columns of IB zero
         const auto rv = buf_rsrc(p.v + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, 2));
 #pragma unroll
@@ -808,46 +829,56 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                 const int ks = sl >> 1;
                 if (sl & 1) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
                 else f.kd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + ks * 1024);
-            } else if (sl < 8 + 4 * NT) {
-                const int e = sl - 8;
-                f.v[e >> 2][e & 3] = __builtin_amdgcn_raw_buffer_load_b16(rv, v_off[e >> 2][e & 3], 0, 0);
+            } else if (sl == 8) {
+                f.x = buf_ld16<u32x4>(x_is_v ? rv : rr, x_off, 0);
+            } else if (sl < 11) {
+                f.ib[sl - 9] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 9) * 1024);
+            } else if (sl < 15) {
+                f.kr[(sl - 11) >> 1][(sl - 11) & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + (sl - 11) * 1024);
             } else {
-                const int e = sl - 8 - 4 * NT;
-                if (e < 2) f.ib[e] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + e * 1024);
-                // gamma for channels 32w + 16rt + 4lq .. +3 and d for rows tb + 4lq .. +3
-                else if (e < 4) f.gam[e - 2] = buf_ld16<f32x4>(rr, r_gam, Rec::GAM + (e - 2) * 64);
-                else if (e < 8) f.kr[(e - 4) >> 1][(e - 4) & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + (e - 4) * 1024);
-                else if (e < 10) f.mq[e - 8] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + (e - 8) * 1024);
-                else f.dg = buf_ld16<f32x4>(rr, r_dg, Rec::DG);
+                f.mq[sl - 15] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + (sl - 15) * 1024);
             }
             // keep the slot order: the in-order vmcnt then lets each use wait
             // for its own load only
             __builtin_amdgcn_sched_barrier(0x048F);
         }
     };
-    // where a step issues the next operands: Kd, Qd and V before its first
-    // product (START), IB and gamma after the first k-step of U (U0), Kr, Mqk
-    // and d after the first k-step of the state update (M0). Issued all at
-    // once, the 23 loads stall the wave on a full vector-memory queue.
+    // where a step issues the next operands: Kd, Qd and the V / gamma piece before
+    // its first product (START), IB after the first k-step of U (U0), Kr and Mqk
+    // after the first k-step of the state update (M0)
     enum { START, U0, M0 };
     auto issue_at = [&](int nj, Frags &nf, int point) {
-        constexpr int NV = 8 + 4 * NT;        // Kd, Qd and V
-        const int a = point == START ? 0 : point == U0 ? NV : NV + 4;
-        const int b = point == START ? NV : point == U0 ? NV + 4 : NLD;
+        const int a = point == START ? 0 : point == U0 ? 9 : 11;
+        const int b = point == START ? 9 : point == U0 ? 11 : NLD;
         issue(nj, nf, a, b);
         // the loads stay where they are issued; compute and LDS traffic may cross
         __builtin_amdgcn_sched_barrier(0x048F);
     };
+    // the V / gamma piece of chunk j into LDS buffer j & 1 (read during step j)
+    auto stage = [&](const Frags &f, int j) {
+        const int bsel = j & 1;
+        if (x_is_v) {
+            // transposed into [col][token]: one column of eight per 16-bit store
+            bf16_t *dst = sV + bsel * TV * SVT + (8 * (tid & 1)) * SVT + (tid >> 1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dst[e * SVT] = static_cast<bf16_t>(e & 1 ? f.x[e >> 1] >> 16 : f.x[e >> 1] & 0xffffu);
+        } else if (tid < 128 + (C + D) / 4) {
+            *reinterpret_cast<u32x4 *>(sDG + bsel * (C + D) + 4 * (tid - 128)) = f.x;
+        }
+    };
 
     // Three operand buffers, used round-robin without copies: the loads for a chunk
-    // are issued two chunks before it is consumed.
-    auto step = [&](const Frags &f, int j, Frags &nf, int nj) {
+    // are issued two chunks before it is consumed, and its V / gamma piece is put
+    // in LDS during the step before.
+    auto step = [&](const Frags &f, int j, const Frags &f1, Frags &nf, int nj) {
         const int tok0 = start + j * C, Lc = min(C, end - tok0);
         const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, sizeof(TO)));
         issue_at(nj, nf, START);
+        const int bsel = j & 1;
 
-        // X = Kd M and O = Qd M for tokens tb..tb+15 (state split hi + lo)
-        f32x4 accX[NT], accO[NT], Ureg[NT];
+        // X = Kd M for tokens tb..tb+15 (state split hi + lo); O^T = M^T Qd^T
+        f32x4 accX[NT], accO[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -857,25 +888,30 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                 const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
                 const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
                 accX[nt] = mfma_f16(f.kd[ks], bh, accX[nt]);
-                accO[nt] = mfma_f16(f.qd[ks], bh, accO[nt]);
+                accO[nt] = mfma_f16(bh, f.qd[ks], accO[nt]);
 #if KDA_SPLIT_X
                 accX[nt] = mfma_f16(f.kd[ks], bl, accX[nt]);
 #endif
 #if KDA_SPLIT_OI
-                accO[nt] = mfma_f16(f.qd[ks], bl, accO[nt]);
+                accO[nt] = mfma_f16(bl, f.qd[ks], accO[nt]);
 #endif
             }
+            // V of tokens tb + 4lq .. +3 at this lane's column
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 vv = *reinterpret_cast<const u32x2 *>(sV + bsel * TV * SVT + (16 * nt + l16) * SVT + tb + 4 * lq);
             f16x4 hi, lo;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float vv = __uint_as_float(f.v[nt][i] << 16);
-                SPLITH(vv - accX[nt][i], hi[i], lo[i]);
+                const uint32_t w = vv[i >> 1];
+                const float v = __uint_as_float(i & 1 ? w & 0xffff0000u : w << 16);
+                SPLITH(v - accX[nt][i], hi[i], lo[i]);
             }
             const int col = 16 * nt + l16, t = tb + 4 * lq;
             *reinterpret_cast<f16x4 *>(sYh + col * SYU + t) = hi;
             *reinterpret_cast<f16x4 *>(sYl + col * SYU + t) = lo;
         }
         __syncthreads();
+        stage(f1, j + 1);
         // U = IB Y (Y split hi + lo)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -890,10 +926,12 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
 #endif
                 if (nt == 0 && ks == 0) issue_at(nj, nf, U0);
             }
-            Ureg[nt] = u;
             f16x4 hi, lo;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) SPLITH(u[i], hi[i], lo[i]);
+            for (int i = 0; i < 4; ++i) {
+                SPLITH(u[i], hi[i], lo[i]);
+                sUf[(tb + 4 * lq + i) * TV + 16 * nt + l16] = u[i];    // fp32 U for d U in the output
+            }
             const int col = 16 * nt + l16, t = tb + 4 * lq;
             *reinterpret_cast<f16x4 *>(sUh + col * SYU + t) = hi;
             *reinterpret_cast<f16x4 *>(sUl + col * SYU + t) = lo;
@@ -903,9 +941,11 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
         for (int nt = 0; nt < NT; ++nt) {
             // M = Diag(gamma) M + Kr^T U for channels 32w..32w+31
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt) {
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(sDG + bsel * (C + D) + C + 32 * wave + 16 * rt + 4 * lq);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Macc[rt][nt][i] *= f.gam[rt][i];
+                for (int i = 0; i < 4; ++i) Macc[rt][nt][i] *= gm[i];
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const f16x8 bh = lds8h(sUh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
@@ -917,17 +957,20 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
                     Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bl, Macc[rt][nt]);
 #endif
                 }
-                // O += Mqk (strictly lower) U
-                accO[nt] = mfma_f16(f.mq[ks], bh, accO[nt]);
+                // O^T += U^T Mqk^T (Mqk strictly lower)
+                accO[nt] = mfma_f16(bh, f.mq[ks], accO[nt]);
 #if KDA_SPLIT_UO
-                accO[nt] = mfma_f16(f.mq[ks], bl, accO[nt]);
+                accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
 #endif
                 if (nt == 0 && ks == 0) issue_at(nj, nf, M0);
             }
-            // + diag(q.k) U with U in fp32, then store (rows past the end are dropped)
+            // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3; one vector
+            // store (rows past the end are dropped)
+            const f32x4 uf = *reinterpret_cast<const f32x4 *>(sUf + (tb + l16) * TV + 16 * nt + 4 * lq);
+            const float dt = sDG[bsel * (C + D) + tb + l16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                buf_st<TO>(ro, v_off[nt][i] * (int)(sizeof(TO) / 2), accO[nt][i] + f.dg[i] * Ureg[nt][i]);
+            for (int i = 0; i < 4; ++i) accO[nt][i] += dt * uf[i];
+            buf_st4<TO>(ro, o_off + 16 * nt * (int)sizeof(TO), accO[nt]);
         }
         if (float *sp = p.snap.slot(n, h, H, j + 1, end - start, C, D * D)) {   // uniform across the workgroup
 #pragma unroll
@@ -952,26 +995,19 @@ __global__ __launch_bounds__(NTHR) void chunk_scan_kernel(ScanParams p) {
         const int last = nch - 1;
         issue(0, A, 0, NLD);
         issue(min(1, last), B, 0, NLD);
+        stage(A, 0);
+        __syncthreads();
         for (int j = 0; j < nch; j += 3) {
-            step(A, j, Cb, min(j + 2, last));
+            step(A, j, B, Cb, min(j + 2, last));
             if (j + 1 >= nch) break;
-            step(B, j + 1, A, min(j + 3, last));
+            step(B, j + 1, Cb, A, min(j + 3, last));
             if (j + 2 >= nch) break;
-            step(Cb, j + 2, B, min(j + 4, last));
+            step(Cb, j + 2, A, B, min(j + 4, last));
         }
     }
 #else
     // two operand buffers: a chunk's loads are issued during the step before it
-    Frags A, B;
-    if (nch > 0) {
-        const int last = nch - 1;
-        issue(0, A, 0, NLD);
-        for (int j = 0; j < nch; j += 2) {
-            step(A, j, B, min(j + 1, last));
-            if (j + 1 >= nch) break;
-            step(B, j + 1, A, min(j + 2, last));
-        }
-    }
+#error "the V / gamma staging needs the next chunk's operands during a step: KDA_SCAN_BUFS must be 3"
 #endif
 
     if (p.S_out) {

@@ -22,8 +22,8 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers, dense and contiguous, in the
- *     layouts given below; q, k, v and g of kda_prefill must be 16-byte
- *     aligned. The caller owns every buffer; the library never allocates or
+ *     layouts given below; q, k, v, g and out of kda_prefill must be
+ *     16-byte aligned. The caller owns every buffer; the library never allocates or
  *     frees device memory and keeps no mutable global state.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream). Nothing is synchronised and no device memory is read on the
