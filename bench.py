@@ -222,6 +222,7 @@ def main():
     line["output_gate"] = {"shape": [pf["tokens"], w_h, w["D"]], "ms_per_call": round(og["ms"], 4),
                            "roofline": {"bound": "hbm", "achieved": round(og["gbps"], 1), "peak": peak_bw,
                                         "unit": "GB/s", "frac": round(og["gbps"] / peak_bw, 4),
+                                        "traffic": measured_traffic("kda_output_gate", args.workload),
                                         "model": "read o and gate, write out (bf16), once each"}}
     if cpu is not None:
         line["cpu_baseline"] = cpu
