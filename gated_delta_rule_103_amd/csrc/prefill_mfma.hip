@@ -563,6 +563,32 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // every later row at once, so the updates of a step are independent and the
         // L column reads (wave-uniform addresses) do not wait on the arithmetic.
         // Entries above the diagonal stay 0 (they only ever see x[sc] = 0).
+        // Meanwhile waves 4-7, idle until the record, build their role's Kd and
+        // Qd fragments (which do not depend on the inverse) and keep them in
+        // registers until the record is stored. (Qd moved into the first
+        // inverse level measured slower: that level then set the pace.)
+        f16x8 fr[8];
+        // x_t e^{a_t} (Kd from k, Qd from q) for the role's 16 tokens as four fp16
+        // A fragments: the chunk-start decay is G (chunk start -> block start)
+        // times E (block start -> t); rs: 1 / ||x_t|| (normalised input) or null
+        auto build_decayed = [&](const __bf16 *sx, const float *rs, f16x8 *dst) {
+            const int role = wave & 3, t = 16 * role + l16;
+            const float nr = NORM ? rs[t] : 1.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 32 * ks + 8 * lq;
+                const bf16x8 xv = lds8(sx + t * SQ + c0);
+                const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + role * D + c0);
+                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + role * D + c0 + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
+                    dst[ks][e] = static_cast<_Float16>((NORM ? bf2f(xv[e]) * nr : bf2f(xv[e])) * dec);
+                }
+            }
+        };
         if (wave < 4 && lane < 16) {
             const int I = wave, col = lane;
             float x[16];
@@ -575,6 +601,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
             for (int tr = 0; tr < 16; ++tr)
                 if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
+        } else if (wave >= 4) {
+            build_decayed(sK, NORM ? sRK : nullptr, fr);
+            build_decayed(sQ, NORM ? sRQ : nullptr, fr + 4);
         }
         __syncthreads();
         fetch(next, 2);
@@ -616,34 +645,16 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 
         // ================= record: fp16 fragments of the scan's left operands
         // Record role r = wave & 3 (tokens 16r..16r+15, channels 32r..32r+31).
-        // Waves 0-3 build Kd and Qd; waves 4-7 build Kr^T, IB and Mqk. Both store
-        // eight fragments from the same code after the branch: stores inside
-        // role branches would leave the compiler a path without them, and its
-        // wait for the next item's inputs would then also wait for the stores.
+        // Waves 4-7 built Kd and Qd above; waves 0-3 build Kr^T, IB and Mqk here.
+        // Both store eight fragments from the same code after the branch: stores
+        // inside role branches would leave the compiler a path without them, and
+        // its wait for the next item's inputs would then also wait for the stores.
         {
             const int role = wave & 3;
             const int t = 16 * role + l16;
-            f16x8 fr[8];
             if (wave < 4) {
-                const int I = role;
-                const float nqr = NORM ? sRQ[t] : 1.f, nkr = NORM ? sRK[t] : 1.f;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int c0 = 32 * ks + 8 * lq;
-                    const bf16x8 kx = lds8(sK + t * SQ + c0), qx = lds8(sQ + t * SQ + c0);
-                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-                    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0);
-                    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + I * D + c0 + 4);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
-                        fr[ks][e] = static_cast<_Float16>((NORM ? bf2f(kx[e]) * nkr : bf2f(kx[e])) * dec);
-                        fr[4 + ks][e] = static_cast<_Float16>((NORM ? bf2f(qx[e]) * nqr : bf2f(qx[e])) * dec);
-                    }
-                }
-            } else {
-                // Kr^T fragments (channel rows, tokens 32ks + 8lq .. +7), built by waves 0-3
+                // Kr^T fragments (channel rows, tokens 32ks + 8lq .. +7), from the
+                // channel-major tile written during the L / Mqk phase
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -664,12 +675,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     fr[6 + ks] = *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
                 }
             }
-            // fragment i: waves 0-3 Kd (i < 4) and Qd, contiguous from KD; waves 4-7
+            // fragment i: waves 4-7 Kd (i < 4) and Qd, contiguous from KD; waves 0-3
             // Kr (i < 4), then IB and Mqk, contiguous from IB
             static_assert(Rec::QD == Rec::KD + 4096 && Rec::MQ == Rec::IB + 2048, "record layout");
             char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES;
             char *rw = rec + (size_t)role * Rec::WAVE + lane * 16;
-            const int o_lo = wave < 4 ? Rec::KD : Rec::KR, o_hi = wave < 4 ? Rec::KD : Rec::IB - 4096;
+            const int o_lo = wave >= 4 ? Rec::KD : Rec::KR, o_hi = wave >= 4 ? Rec::KD : Rec::IB - 4096;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 *reinterpret_cast<f16x8 *>(rw + (i < 4 ? o_lo : o_hi) + i * 1024) = fr[i];
