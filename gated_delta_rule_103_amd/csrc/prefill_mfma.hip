@@ -752,7 +752,8 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     using Lo = ScanLds<TV>;
     constexpr int NT = TV / 16;
     constexpr int TEAM = D / TV;
-    static_assert(NT == 1, "one 16-column tile per workgroup: the V tile is staged by 128 lanes of 16 bytes");
+    static_assert(TV == 16 || TV == 32, "value columns per workgroup");
+    constexpr int XP = NT;               // 16-byte pieces of V, d and gamma per lane and chunk
     _Float16 *sMh = reinterpret_cast<_Float16 *>(smem + Lo::M);
     _Float16 *sMl = sMh + TV * SMS;
     _Float16 *sYh = reinterpret_cast<_Float16 *>(smem + Lo::Y);
@@ -808,18 +809,23 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     // operands of one chunk, loaded two chunks ahead
     struct Frags {
         f16x8 kd[4], qd[4], ib[2], mq[2], kr[2][2];
-        // one 16-byte piece of the chunk's V tile (waves 0-1: token (tid >> 1),
-        // columns 8 (tid & 1) .. +7) or of its d and gamma, which are adjacent in
-        // the record (waves 2-3: floats 4 (tid - 128) .. +3 of the 192; lanes past
-        // them repeat the last piece), staged through LDS one chunk ahead
-        u32x4 x;
+        // 16-byte pieces of the chunk's V tile and of its d and gamma (adjacent in
+        // the record, 192 floats), staged through LDS one chunk ahead. TV = 16:
+        // one piece, waves 0-1 V (token tid >> 1, columns 8 (tid & 1) .. +7), waves
+        // 2-3 d and gamma (floats 4 (tid - 128) .. +3; lanes past them repeat the
+        // last piece). TV = 32: piece 0 V (token tid >> 2, columns 8 (tid & 3) ..
+        // +7), piece 1 d and gamma (floats 4 tid .. +3, repeated past them).
+        u32x4 x[XP];
     };
     // loop-invariant byte offsets of this lane's record fragments
     const int r_frag = wave * Rec::WAVE + lane * 16;
-    const bool x_is_v = wave < 2;                                  // uniform
+    const bool x_is_v = TV == 32 || wave < 2;                      // uniform (piece 0)
     static_assert(Rec::GAM == Rec::DG + C * 4, "d and gamma adjacent in the record");
-    const int x_off = x_is_v ? ((tid >> 1) * H * D + col0 + 8 * (tid & 1)) * 2
-                             : Rec::DG + 16 * min(tid - 128, (C + D) / 4 - 1);
+    constexpr int VL = TV / 8;                                     // lanes per V row
+    int x_off[XP];
+    x_off[0] = x_is_v ? ((tid / VL) * H * D + col0 + 8 * (tid % VL)) * 2
+                      : Rec::DG + 16 * min(tid - 128, (C + D) / 4 - 1);
+    if constexpr (XP == 2) x_off[XP - 1] = Rec::DG + 16 * min(tid, (C + D) / 4 - 1);
     // this lane's output: token tb + l16, columns col0 + 4lq .. +3 (O is formed transposed)
     const int o_off = ((tb + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
     // bytes from a chunk's first row to the end of its last valid row
@@ -829,7 +835,7 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     // consumed: Kd and Qd by k-step, the V / gamma piece, IB, Kr, Mqk. issue()
     // sends slots [s0, s1); the step spreads them over its phases, so that no
     // wave stalls on a full vector-memory queue with work of its own waiting.
-    constexpr int NLD = 17;
+    constexpr int NLD = 16 + XP;
     auto issue = [&](int j, Frags &f, int s0, int s1) {
         const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
         const int tok0 = start + j * C, Lc = min(C, end - tok0);
@@ -843,14 +849,16 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
                 const int ks = sl >> 1;
                 if (sl & 1) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
                 else f.kd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + ks * 1024);
-            } else if (sl == 8) {
-                f.x = buf_ld16<u32x4>(x_is_v ? rv : rr, x_off, 0);
-            } else if (sl < 11) {
-                f.ib[sl - 9] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 9) * 1024);
-            } else if (sl < 15) {
-                f.kr[(sl - 11) >> 1][(sl - 11) & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + (sl - 11) * 1024);
+            } else if (sl < 8 + XP) {
+                const int pc = sl - 8;
+                f.x[pc] = buf_ld16<u32x4>(pc == 0 && x_is_v ? rv : rr, x_off[pc], 0);
+            } else if (sl < 10 + XP) {
+                f.ib[sl - 8 - XP] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 8 - XP) * 1024);
+            } else if (sl < 14 + XP) {
+                const int e = sl - 10 - XP;
+                f.kr[e >> 1][e & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + e * 1024);
             } else {
-                f.mq[sl - 15] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + (sl - 15) * 1024);
+                f.mq[sl - 14 - XP] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + (sl - 14 - XP) * 1024);
             }
             // keep the slot order: the in-order vmcnt then lets each use wait
             // for its own load only
@@ -862,8 +870,8 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     // after the first k-step of the state update (M0)
     enum { START, U0, M0 };
     auto issue_at = [&](int nj, Frags &nf, int point) {
-        const int a = point == START ? 0 : point == U0 ? 9 : 11;
-        const int b = point == START ? 9 : point == U0 ? 11 : NLD;
+        const int a = point == START ? 0 : point == U0 ? 8 + XP : 10 + XP;
+        const int b = point == START ? 8 + XP : point == U0 ? 10 + XP : NLD;
         issue(nj, nf, a, b);
         // the loads stay where they are issued; compute and LDS traffic may cross
         __builtin_amdgcn_sched_barrier(0x048F);
@@ -873,13 +881,14 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
         const int bsel = j & 1;
         if (x_is_v) {
             // transposed into [col][token]: one column of eight per 16-bit store
-            bf16_t *dst = sV + bsel * TV * SVT + (8 * (tid & 1)) * SVT + (tid >> 1);
+            bf16_t *dst = sV + bsel * TV * SVT + (8 * (tid % VL)) * SVT + (tid / VL);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                dst[e * SVT] = static_cast<bf16_t>(e & 1 ? f.x[e >> 1] >> 16 : f.x[e >> 1] & 0xffffu);
-        } else if (tid < 128 + (C + D) / 4) {
-            *reinterpret_cast<u32x4 *>(sDG + bsel * (C + D) + 4 * (tid - 128)) = f.x;
+                dst[e * SVT] = static_cast<bf16_t>(e & 1 ? f.x[0][e >> 1] >> 16 : f.x[0][e >> 1] & 0xffffu);
         }
+        const int dl = XP == 2 ? tid : tid - 128;                  // lane's d / gamma piece
+        if ((XP == 2 || !x_is_v) && dl < (C + D) / 4)
+            *reinterpret_cast<u32x4 *>(sDG + bsel * (C + D) + 4 * dl) = f.x[XP - 1];
     };
 
     // Three operand buffers, used round-robin without copies: the loads for a chunk
@@ -1038,7 +1047,6 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
 }
 
 // ---------------------------------------------------------------- host
-constexpr int kTV = 16;
 // persistent prep: one workgroup per compute unit (its LDS use allows one)
 long long prep_grid() {
     static int cus = 0;
@@ -1102,13 +1110,19 @@ hipError_t run(const PrefillArgs &a) {
         }
     }
     {
-        constexpr int TEAM = D / kTV;
-        auto kern = chunk_scan_kernel<kTV, TO>;
+        // 16 value columns per workgroup, or 32 when the 16-column workgroups would
+        // fill the CUs four times over or more (many chains, e.g. packed batches):
+        // a CU then reads each record once per 32 columns instead of per 16
         const int chains = a.N * a.H;
-        const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * TEAM;
+        const bool wide = (long long)chains * (D / 16) >= 4 * prep_grid();
+        const int team = wide ? D / 32 : D / 16;
+        const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
         ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc,
                       SnapView{a.snaps, a.snap_every, a.max_snaps}};
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(NTHR), ScanLds<kTV>::SIZE, a.stream, sp);
+        if (wide)
+            hipLaunchKernelGGL((chunk_scan_kernel<32, TO>), dim3(blocks), dim3(NTHR), ScanLds<32>::SIZE, a.stream, sp);
+        else
+            hipLaunchKernelGGL((chunk_scan_kernel<16, TO>), dim3(blocks), dim3(NTHR), ScanLds<16>::SIZE, a.stream, sp);
         return hipGetLastError();
     }
 }

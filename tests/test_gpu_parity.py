@@ -148,6 +148,18 @@ def test_prefill_ragged_lengths(D, C, io):
         run_and_check(p, tol, label=f"dense T={T}")
 
 
+@pytest.mark.parametrize("slow", [False, True])
+def test_prefill_many_chains_wide_scan_tiles(slow):
+    """Packed batches with many (sequence, head) chains take the scan's 32-column
+    workgroups (chains x 8 >= 4 x CUs): 12 ragged sequences x 16 heads = 192
+    chains, nonzero S0, a zero-length and a one-token sequence among them, and a
+    slow-decay variant where the state carries across chunks."""
+    lengths = [130, 0, 64, 1, 257, 191, 65, 128, 320, 63, 200, 96]
+    p = inputs.prefill(16, 128, lengths=lengths, C=64, io="bf16", s0_std=0.3, seed=41,
+                       shift=-4.0 if slow else 2.0)
+    run_and_check(p, TOL_BF16, label=f"many chains, wide scan tiles{' (slow decay)' if slow else ''}")
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_prefill_varlen_edges(io):
     """Packed sequences with zero- and one-token members and a nonzero initial state."""
