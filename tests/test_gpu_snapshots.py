@@ -79,6 +79,13 @@ def test_snapshots_varlen_bf16_mfma_with_state():
     _check(p, 64, 10, TOL_BF16, "varlen bf16 with S0, slow decay")
 
 
+def test_snapshots_many_chains_wide_scan_tiles():
+    """192 chains (12 packed sequences x 16 heads) take the scan's 32-column workgroups."""
+    p = inputs.prefill(16, 128, lengths=[130, 0, 64, 1, 257, 191, 65, 128, 320, 63, 200, 96], C=64,
+                       io="bf16", s0_std=0.02, gate="slow", seed=75)
+    _check(p, 64, 4, TOL_BF16, "many chains, wide scan tiles")
+
+
 def test_snapshots_f32_path():
     p = inputs.prefill(2, 64, B=1, T=150, C=16, io="f32", seed=73)
     _check(p, 32, 6, TOL_F32, "fp32 path, D=64, C=16")
