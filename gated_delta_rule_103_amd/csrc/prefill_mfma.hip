@@ -161,8 +161,8 @@ struct PrepLds {
     static constexpr int RQ = GAM + D * 4;           // fp32 [64] 1 / ||q_t|| (L2-normalised input)
     static constexpr int RK = RQ + C * 4;            // fp32 [64] 1 / ||k_t||
     static constexpr int FLAG = RK + C * 4;          // int [4]
-    static constexpr int T3 = FLAG + 16;             // fp32 [3][256] inverse scratch
-    static constexpr int KRT = T3 + 3 * 256 * 4;     // fp16 [128][SKR] Kr^T, channel-major
+    static constexpr int T3 = FLAG + 16;             // fp32 [4][256] inverse scratch
+    static constexpr int KRT = T3 + 4 * 256 * 4;     // fp16 [128][SKR] Kr^T, channel-major
     static constexpr int SIZE = KRT + D * SKR * 2;
 };
 
@@ -610,24 +610,30 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         }
         __syncthreads();
         fetch(next, 2);
-        // off-diagonal blocks, one level (I - J) at a time, on fp32 MFMA (exact products):
-        //   T = sum_{K=J}^{I-1} L_IK INV_KJ ;  INV_IJ = -INV_II T
+        // off-diagonal blocks on fp32 MFMA (exact products), with the 64 x 64 inverse
+        // taken as 2 x 2 blocks of 32 (A, D its diagonal halves, C = L[32:64][0:32]):
+        //   stage 1:  INV_10 = -INV_11 L_10 INV_00,  INV_32 = -INV_33 L_32 INV_22
+        //   stage 2a: P = C A^{-1}    (P_IJ = sum_{J<=K<=1} L_IK INV_KJ, I in {2,3}, J in {0,1})
+        //   stage 2b: INV_IJ = -sum_{2<=K<=I} INV_IK P_KJ
+        // Four dependent products on the critical path instead of six for three
+        // levels of INV_IJ = -INV_II sum_K L_IK INV_KJ. Operands: a 16x16x4 fragment
+        // gives lane (l16, lq) A[row = l16][k] and B[k][col = l16], k = 4 sl + lq.
         // INV_XY[a][b] lives at sLI[(16Y + b) * SL + 16X + a]; for X == Y only a >= b is stored.
-        for (int lev = 1; lev < 4; ++lev) {
-            if (wave < 4 - lev) {
-                const int J = wave, I = J + lev;
-                const int row = l16, kk = lq;          // 16x16x4 fragment: lane -> (row/col, k)
+        {
+            const int row = l16, kk = lq;
+            // INV_XY[r][c] (X >= Y, zero above the diagonal of a diagonal block)
+            auto inv_at = [&](int X, int Y, int r, int c) {
+                return (X == Y && c > r) ? 0.f : sLI[(16 * Y + c) * SL + 16 * X + r];
+            };
+            if (wave < 2) {                                     // stage 1
+                const int J = 2 * wave, I = J + 1;
                 f32x4 T4 = {0.f, 0.f, 0.f, 0.f};
-                for (int K2 = J; K2 < I; ++K2) {
 #pragma unroll
-                    for (int sl = 0; sl < 4; ++sl) {
-                        const int k = 4 * sl + kk;
-                        const float a = sLI[(16 * I + row) * SL + 16 * K2 + k];                  // L_IK[row][k]
-                        const float bv = (K2 == J && k < row) ? 0.f : sLI[(16 * J + row) * SL + 16 * K2 + k];  // INV_KJ[k][col=row]
-                        T4 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, T4, 0, 0, 0);
-                    }
+                for (int sl = 0; sl < 4; ++sl) {
+                    const int k = 4 * sl + kk;
+                    T4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sLI[(16 * I + row) * SL + 16 * J + k],   // L_IJ[row][k]
+                                                              inv_at(J, J, k, row), T4, 0, 0, 0);      // INV_JJ[k][col]
                 }
-                // T (lane: col l16, rows 4lq..4lq+3) -> scratch [row][col] for the B operand
                 float *tw = sT3 + wave * 256;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tw[(4 * lq + i) * 16 + l16] = T4[i];
@@ -636,9 +642,40 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {
                     const int k = 4 * sl + kk;
-                    const float a = (row >= k) ? sLI[(16 * I + k) * SL + 16 * I + row] : 0.f;   // INV_II[row][k]
-                    const float bv = tw[k * 16 + l16];                                           // T[k][col]
-                    O4 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, O4, 0, 0, 0);
+                    O4 = __builtin_amdgcn_mfma_f32_16x16x4f32(inv_at(I, I, row, k), tw[k * 16 + l16], O4, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -O4[i];
+            }
+            __syncthreads();
+            // stage 2a: wave w < 4 takes P_IJ with I = 2 + (w >> 1), J = w & 1
+            if (wave < 4) {
+                const int I = 2 + (wave >> 1), J = wave & 1;
+                f32x4 P4 = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < 2; ++K) {
+#pragma unroll
+                    for (int sl = 0; sl < 4; ++sl) {
+                        const int k = 4 * sl + kk;
+                        P4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sLI[(16 * I + row) * SL + 16 * K + k],  // L_IK[row][k]
+                                                                  inv_at(K, J, k, row), P4, 0, 0, 0);     // INV_KJ[k][col]
+                    }
+                }
+                float *pw = sT3 + wave * 256;                   // P_IJ, [row][col]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pw[(4 * lq + i) * 16 + l16] = P4[i];
+            }
+            __syncthreads();
+            // stage 2b: wave w < 4 takes INV_IJ with I = 2 + (w >> 1), J = w & 1
+            if (wave < 4) {
+                const int I = 2 + (wave >> 1), J = wave & 1;
+                f32x4 O4 = {0.f, 0.f, 0.f, 0.f};
+                for (int K = 2; K <= I; ++K) {
+                    const float *pk = sT3 + ((K - 2) * 2 + J) * 256;    // P_KJ
+#pragma unroll
+                    for (int sl = 0; sl < 4; ++sl) {
+                        const int k = 4 * sl + kk;
+                        O4 = __builtin_amdgcn_mfma_f32_16x16x4f32(inv_at(I, K, row, k), pk[k * 16 + l16], O4, 0, 0, 0);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -O4[i];
