@@ -31,14 +31,26 @@ DECODE_WORKLOAD = "decode_512x32"
 PREFILL_DTYPE = "bf16"
 
 
+# Every leg's untimed warmup lasts at least this long (and at least `warmup`
+# calls): a few calls after start-up run several percent slower than the
+# steady state the timed region is meant to measure.
+WARMUP_MIN_S = 0.25
+
+
 def _time_region(fn, steps, warmup):
-    """Run warmup untimed, then time exactly `steps` back-to-back calls,
-    synchronised on both sides: host wall clock for the region, and one pair
-    of events on the current stream (the one the library launches on)
-    bracketing the same calls, whose elapsed time / steps is the average device
-    duration of one call. Events between calls would add a gap to every call."""
-    for _ in range(warmup):
+    """Run warmup untimed (at least `warmup` calls and WARMUP_MIN_S seconds),
+    then time exactly `steps` back-to-back calls, synchronised on both sides:
+    host wall clock for the region, and one pair of events on the current
+    stream (the one the library launches on) bracketing the same calls, whose
+    elapsed time / steps is the average device duration of one call. Events
+    between calls would add a gap to every call."""
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
         fn()
+        done += 1
+        if done % 16 == 0:
+            torch.cuda.synchronize()       # the host clock then tracks the device
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -191,6 +203,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": WARMUP_MIN_S,
         "ms_per_step": round(pf["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
