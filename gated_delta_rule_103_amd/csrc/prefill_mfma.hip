@@ -139,6 +139,7 @@ struct Rec {
 };
 
 // ---------------------------------------------------------------- prep
+template <int N> struct IC { static constexpr int value = N; };    // an int as a type (compile-time argument)
 constexpr int PTHR = 512;        // prep: 8 wavefronts, two per SIMD to hide latency
 constexpr int SQ = D + 8;        // bf16 row stride of q, k           [64][136]
 constexpr int SE = D + 4;        // fp32 row stride of the decays     [64][132]
@@ -467,62 +468,66 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 sMqk[(16 * I2 + (e >> 4)) * SMQ + 16 * J2 + (e & 15)] = static_cast<_Float16>(0.f);
             }
         } else {
-            const int I = wave == 6 ? 2 : wave == 7 ? 1 : 3;
-            const int nb = (wave == 5 || wave == 7) ? 1 : 2;
-            const int J0 = wave == 5 ? 2 : 0, J1 = 1;
-            f32x4 accL[2], accM[2];
+            // the wavefront's blocks (I, J0) and, when NB = 2, (I, 1), with the block
+            // indices known at compile time: the decay factors between the blocks and
+            // the loop bounds then cost no selects, multiplications by one or branches
+            auto offdiag = [&](auto Ic, auto J0c, auto NBc) {
+                constexpr int I = decltype(Ic)::value, J0 = decltype(J0c)::value, NB = decltype(NBc)::value;
+                f32x4 accL[NB], accM[NB];
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) { accL[bb] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[bb] = accL[bb]; }
-            const int t = 16 * I + l16;
-            const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
+                for (int bb = 0; bb < NB; ++bb) { accL[bb] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[bb] = accL[bb]; }
+                const int t = 16 * I + l16;
+                const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int c0 = 32 * ks + 8 * lq;
-                const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
-                const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-                f16x8 aq, ak;
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int c0 = 32 * ks + 8 * lq;
+                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
+                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    f16x8 aq, ak;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float fa = e < 4 ? a0[e] : a1[e - 4];
-                    aq[e] = static_cast<_Float16>(NORM ? bf2f(qv[e]) * nq * fa : bf2f(qv[e]) * fa);
-                    ak[e] = static_cast<_Float16>(NORM ? bf2f(kv[e]) * nk * fa : bf2f(kv[e]) * fa);
+                    for (int e = 0; e < 8; ++e) {
+                        const float fa = e < 4 ? a0[e] : a1[e - 4];
+                        aq[e] = static_cast<_Float16>(NORM ? bf2f(qv[e]) * nq * fa : bf2f(qv[e]) * fa);
+                        ak[e] = static_cast<_Float16>(NORM ? bf2f(kv[e]) * nk * fa : bf2f(kv[e]) * fa);
+                    }
+#pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) {
+                        const int J = bb ? 1 : J0, sr = 16 * J + l16;
+                        const bf16x8 sv = lds8(sK + sr * SQ + c0);
+                        f32x4 b0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
+                        f32x4 b1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
+                        // prod_{J<K<I} Gamma_K (none for adjacent blocks)
+#pragma unroll
+                        for (int K = J + 1; K < I; ++K) {
+                            b0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
+                            b1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
+                        }
+                        const float ns = NORM ? sRK[sr] : 1.f;
+                        f16x8 bk;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            bk[e] = static_cast<_Float16>((NORM ? bf2f(sv[e]) * ns : bf2f(sv[e])) * (e < 4 ? b0[e] : b1[e - 4]));
+                        accL[bb] = mfma_f16(ak, bk, accL[bb]);
+                        accM[bb] = mfma_f16(aq, bk, accM[bb]);
+                    }
                 }
 #pragma unroll
-                for (int bb = 0; bb < 2; ++bb) {
-                    if (bb >= nb) break;                     // uniform across the wavefront
-                    const int J = bb ? J1 : J0, sr = 16 * J + l16;
-                    const bf16x8 sv = lds8(sK + sr * SQ + c0);
-                    f32x4 b0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
-                    f32x4 b1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
-                    // prod_{J<K<I} Gamma_K, at most two factors (I - J <= 3); both rows
-                    // are read unconditionally (clamped) and unused factors are ones
-                    const float *gA = sGB + (J + 1) * D + c0, *gB = sGB + min(J + 2, 3) * D + c0;
-                    const f32x4 one = {1.f, 1.f, 1.f, 1.f};
-                    const f32x4 a0v = *reinterpret_cast<const f32x4 *>(gA), a1v = *reinterpret_cast<const f32x4 *>(gA + 4);
-                    const f32x4 c0v = *reinterpret_cast<const f32x4 *>(gB), c1v = *reinterpret_cast<const f32x4 *>(gB + 4);
-                    b0 *= (I - J >= 2 ? a0v : one) * (I - J == 3 ? c0v : one);
-                    b1 *= (I - J >= 2 ? a1v : one) * (I - J == 3 ? c1v : one);
-                    const float ns = NORM ? sRK[sr] : 1.f;
-                    f16x8 bk;
+                for (int bb = 0; bb < NB; ++bb) {
+                    const int J = bb ? 1 : J0;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        bk[e] = static_cast<_Float16>((NORM ? bf2f(sv[e]) * ns : bf2f(sv[e])) * (e < 4 ? b0[e] : b1[e - 4]));
-                    accL[bb] = mfma_f16(ak, bk, accL[bb]);
-                    accM[bb] = mfma_f16(aq, bk, accM[bb]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int tr = 16 * I + 4 * lq + i, sc = 16 * J + l16;
+                        sLI[tr * SL + sc] = sBeta[tr] * accL[bb][i];
+                        sMqk[tr * SMQ + sc] = static_cast<_Float16>(accM[bb][i]);
+                    }
                 }
-            }
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                if (bb >= nb) break;
-                const int J = bb ? J1 : J0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tr = 16 * I + 4 * lq + i, sc = 16 * J + l16;
-                    sLI[tr * SL + sc] = sBeta[tr] * accL[bb][i];
-                    sMqk[tr * SMQ + sc] = static_cast<_Float16>(accM[bb][i]);
-                }
-            }
+            };
+            //   wavefront 4: (3,0) (3,1)   5: (3,2)   6: (2,0) (2,1)   7: (1,0)
+            if (wave == 4) offdiag(IC<3>{}, IC<0>{}, IC<2>{});
+            else if (wave == 5) offdiag(IC<3>{}, IC<2>{}, IC<1>{});
+            else if (wave == 6) offdiag(IC<2>{}, IC<0>{}, IC<2>{});
+            else offdiag(IC<1>{}, IC<0>{}, IC<1>{});
         }
         // exact path for diagonal blocks whose in-block decay leaves the fp32 normal range
         for (int I = 0; I < 4 && (flags.x | flags.y | flags.z | flags.w); ++I) {
