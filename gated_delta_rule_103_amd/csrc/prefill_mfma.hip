@@ -460,13 +460,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 if constexpr (NORM) acc *= sRQ[row] * sRK[row];
                 if (seg == 0) sDg[row] = acc;
             }
-            // zero the upper blocks of Mqk (never written elsewhere)
-            for (int idx = tid; idx < 6 * 256; idx += 256) {
-                const int bb = idx >> 8, e = idx & 255;
-                int I2, J2;
-                if (bb < 3) { I2 = bb; J2 = bb + 1; } else if (bb < 5) { I2 = bb - 3; J2 = I2 + 2; } else { I2 = 0; J2 = 3; }
-                sMqk[(16 * I2 + (e >> 4)) * SMQ + 16 * J2 + (e & 15)] = static_cast<_Float16>(0.f);
-            }
         } else {
             // the wavefront's blocks (I, J0) and, when NB = 2, (I, 1), with the block
             // indices known at compile time: the decay factors between the blocks and
@@ -717,7 +710,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         const float x = sLI[sc * SL + t] * (e < 4 ? be0[e] : be1[e - 4]);
                         fr[4 + ks][e] = static_cast<_Float16>(sc <= t ? x : 0.f);
                     }
-                    fr[6 + ks] = *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
+                    // Mqk blocks above the diagonal block are never written: select zeros
+                    // there (a select, so stale LDS contents cannot leak in)
+                    const f16x8 mq = *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
+                    fr[6 + ks] = 2 * ks + (lq >> 1) > role ? f16x8{} : mq;
                 }
             }
             // fragment i: waves 4-7 Kd (i < 4) and Qd, contiguous from KD; waves 0-3
