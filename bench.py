@@ -33,8 +33,12 @@ PREFILL_DTYPE = "bf16"
 
 # Every leg's untimed warmup lasts at least this long (and at least `warmup`
 # calls): a few calls after start-up run several percent slower than the
-# steady state the timed region is meant to measure.
+# steady state the timed region is meant to measure. --warmup-min-s overrides
+# it (profiler runs, where every call is traced, set 0).
 WARMUP_MIN_S = 0.25
+
+
+_warmup_min_s = WARMUP_MIN_S
 
 
 def _time_region(fn, steps, warmup):
@@ -46,7 +50,7 @@ def _time_region(fn, steps, warmup):
     between calls would add a gap to every call."""
     t_w = time.perf_counter()
     done = 0
-    while done < warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+    while done < warmup or time.perf_counter() - t_w < _warmup_min_s:
         fn()
         done += 1
         if done % 16 == 0:
@@ -169,6 +173,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup-min-s", type=float, default=WARMUP_MIN_S,
+                    help="minimum duration of each leg's untimed warmup, in seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--workload", default=PREFILL_WORKLOAD, choices=["single_seq_8k", "varlen_16x", "long_1m"],
@@ -182,6 +188,8 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    global _warmup_min_s
+    _warmup_min_s = max(0.0, args.warmup_min_s)
 
     pf = bench_prefill(args.steps, args.warmup, args.workload)
     peak_tf = costs.MI355X_PEAK["bf16_TFLOPs"]
@@ -203,7 +211,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_min_s": WARMUP_MIN_S,
+        "warmup_min_s": _warmup_min_s,
         "ms_per_step": round(pf["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
