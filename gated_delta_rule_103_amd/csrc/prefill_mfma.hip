@@ -45,7 +45,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;       // Dk == Dv
 constexpr int C = 64;        // chunk length
-constexpr int NTHR = 256;    // 4 wavefronts, one per SIMD
+constexpr int NTHR = 256;    // scan: 4 recurrence wavefronts, one per SIMD ...
+constexpr int SCAN_THR = 2 * NTHR;   // ... and 4 output wavefronts beside them
 constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 
 // Which right-hand operands of the scan's fp16 contractions are split into
@@ -785,7 +786,7 @@ template <> __device__ __forceinline__ void buf_st4<bf16_t>(__amdgpu_buffer_rsrc
 }
 
 template <int TV, typename TO>
-__global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = ScanLds<TV>;
     constexpr int NT = TV / 16;
@@ -816,7 +817,90 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     const int start = p.sv.seq_start(n), end = p.sv.seq_end(n);
     const int nch = (end - start + C - 1) / C, c0 = p.sv.first_chunk(n);
     const size_t st_off = ((size_t)n * H + h) * D * D;
-    const int tb = 16 * wave;
+    const int tb = 16 * (wave & 3);
+
+    if (wave >= 4) {
+        // Output wavefronts: o = Qd M + Mqk U + d U for token tile tb, from the
+        // state and U that the recurrence wavefronts put in LDS, so that the
+        // recurrence's own steps carry only what the next chunk depends on. Their
+        // operands (Qd, Mqk) are loaded two chunks ahead, like the recurrence's;
+        // they pass the same barriers (one before the first chunk, three per
+        // chunk).
+        struct OFrags {
+            f16x8 qd[4], mq[2];
+        };
+        const int r_frag = (wave & 3) * Rec::WAVE + lane * 16;
+        // this lane's output: token tb + l16, columns col0 + 4lq .. +3 (O is formed transposed)
+        const int o_off = ((tb + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
+        auto oissue = [&](int j, OFrags &f) {
+            const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) f.mq[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + ks * 1024);
+        };
+        auto ostep = [&](const OFrags &f, int j, OFrags &nf, int nj) {
+            oissue(nj, nf);
+            const int tok0 = start + j * C, Lc = min(C, end - tok0);
+            const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D,
+                                     ((Lc - 1) * H * D + D) * (int)sizeof(TO));
+            const int bsel = j & 1;
+            // O^T = M^T Qd^T from the state at the chunk start (published before the
+            // barrier that ended the previous step)
+            f32x4 accO[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
+                    accO[nt] = mfma_f16(bh, f.qd[ks], accO[nt]);
+#if KDA_SPLIT_OI
+                    const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
+                    accO[nt] = mfma_f16(bl, f.qd[ks], accO[nt]);
+#endif
+                }
+            }
+            __syncthreads();     // Y = V - Kd M is in LDS
+            __syncthreads();     // U is in LDS
+            const float dt = sDG[bsel * (C + D) + tb + l16];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    // O^T += U^T Mqk^T (Mqk strictly lower)
+                    const f16x8 bh = lds8h(sUh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+                    accO[nt] = mfma_f16(bh, f.mq[ks], accO[nt]);
+#if KDA_SPLIT_UO
+                    const f16x8 bl = lds8h(sUl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+                    accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
+#endif
+                }
+                // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3; one vector
+                // store (rows past the end are dropped)
+                const f32x4 uf = *reinterpret_cast<const f32x4 *>(sUf + (tb + l16) * TV + 16 * nt + 4 * lq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accO[nt][i] += dt * uf[i];
+                buf_st4<TO>(ro, o_off + 16 * nt * (int)sizeof(TO), accO[nt]);
+            }
+            __syncthreads();     // the next state is in LDS
+        };
+        if (nch > 0) {
+            const int last = nch - 1;
+            OFrags A, B, Cb;
+            oissue(0, A);
+            oissue(min(1, last), B);
+            __syncthreads();     // the initial state is in LDS
+            for (int j = 0; j < nch; j += 3) {
+                ostep(A, j, Cb, min(j + 2, last));
+                if (j + 1 >= nch) break;
+                ostep(B, j + 1, A, min(j + 3, last));
+                if (j + 2 >= nch) break;
+                ostep(Cb, j + 2, B, min(j + 4, last));
+            }
+        }
+        return;
+    }
 
     // state tile: wave w owns channels 32w..32w+31 (two 16-row tiles)
     f32x4 Macc[2][NT];
@@ -846,7 +930,7 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
 
     // operands of one chunk, loaded two chunks ahead
     struct Frags {
-        f16x8 kd[4], qd[4], ib[2], mq[2], kr[2][2];
+        f16x8 kd[4], ib[2], kr[2][2];
         // 16-byte pieces of the chunk's V tile and of its d and gamma (adjacent in
         // the record, 192 floats), staged through LDS one chunk ahead. TV = 16:
         // one piece, waves 0-1 V (token tid >> 1, columns 8 (tid & 1) .. +7), waves
@@ -864,16 +948,14 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     x_off[0] = x_is_v ? ((tid / VL) * H * D + col0 + 8 * (tid % VL)) * 2
                       : Rec::DG + 16 * min(tid - 128, (C + D) / 4 - 1);
     if constexpr (XP == 2) x_off[XP - 1] = Rec::DG + 16 * min(tid, (C + D) / 4 - 1);
-    // this lane's output: token tb + l16, columns col0 + 4lq .. +3 (O is formed transposed)
-    const int o_off = ((tb + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
     // bytes from a chunk's first row to the end of its last valid row
     auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
 
     // The loads of one chunk's operands, as NLD slots in the order they are
-    // consumed: Kd and Qd by k-step, the V / gamma piece, IB, Kr, Mqk. issue()
+    // consumed: Kd by k-step, the V / gamma piece, IB, Kr. issue()
     // sends slots [s0, s1); the step spreads them over its phases, so that no
     // wave stalls on a full vector-memory queue with work of its own waiting.
-    constexpr int NLD = 16 + XP;
+    constexpr int NLD = 10 + XP;
     auto issue = [&](int j, Frags &f, int s0, int s1) {
         const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
         const int tok0 = start + j * C, Lc = min(C, end - tok0);
@@ -883,33 +965,29 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
 #pragma unroll
         for (int sl = 0; sl < NLD; ++sl) {
             if (sl < s0 || sl >= s1) continue;
-            if (sl < 8) {
-                const int ks = sl >> 1;
-                if (sl & 1) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
-                else f.kd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + ks * 1024);
-            } else if (sl < 8 + XP) {
-                const int pc = sl - 8;
+            if (sl < 4) {
+                f.kd[sl] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + sl * 1024);
+            } else if (sl < 4 + XP) {
+                const int pc = sl - 4;
                 f.x[pc] = buf_ld16<u32x4>(pc == 0 && x_is_v ? rv : rr, x_off[pc], 0);
-            } else if (sl < 10 + XP) {
-                f.ib[sl - 8 - XP] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 8 - XP) * 1024);
-            } else if (sl < 14 + XP) {
-                const int e = sl - 10 - XP;
-                f.kr[e >> 1][e & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + e * 1024);
+            } else if (sl < 6 + XP) {
+                f.ib[sl - 4 - XP] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 4 - XP) * 1024);
             } else {
-                f.mq[sl - 14 - XP] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + (sl - 14 - XP) * 1024);
+                const int e = sl - 6 - XP;
+                f.kr[e >> 1][e & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + e * 1024);
             }
             // keep the slot order: the in-order vmcnt then lets each use wait
             // for its own load only
             __builtin_amdgcn_sched_barrier(0x048F);
         }
     };
-    // where a step issues the next operands: Kd, Qd and the V / gamma piece before
-    // its first product (START), IB after the first k-step of U (U0), Kr and Mqk
-    // after the first k-step of the state update (M0)
+    // where a step issues the next operands: Kd and the V / gamma piece before its
+    // first product (START), IB after the first k-step of U (U0), Kr after the
+    // first k-step of the state update (M0)
     enum { START, U0, M0 };
     auto issue_at = [&](int nj, Frags &nf, int point) {
-        const int a = point == START ? 0 : point == U0 ? 8 + XP : 10 + XP;
-        const int b = point == START ? 8 + XP : point == U0 ? 10 + XP : NLD;
+        const int a = point == START ? 0 : point == U0 ? 4 + XP : 6 + XP;
+        const int b = point == START ? 4 + XP : point == U0 ? 6 + XP : NLD;
         issue(nj, nf, a, b);
         // the loads stay where they are issued; compute and LDS traffic may cross
         __builtin_amdgcn_sched_barrier(0x048F);
@@ -933,28 +1011,21 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
     // are issued two chunks before it is consumed, and its V / gamma piece is put
     // in LDS during the step before.
     auto step = [&](const Frags &f, int j, const Frags &f1, Frags &nf, int nj) {
-        const int tok0 = start + j * C, Lc = min(C, end - tok0);
-        const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, sizeof(TO)));
         issue_at(nj, nf, START);
         const int bsel = j & 1;
 
-        // X = Kd M for tokens tb..tb+15 (state split hi + lo); O^T = M^T Qd^T
-        f32x4 accX[NT], accO[NT];
+        // X = Kd M for tokens tb..tb+15 (state split hi + lo)
+        f32x4 accX[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accO[nt] = accX[nt];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
-                const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
                 accX[nt] = mfma_f16(f.kd[ks], bh, accX[nt]);
-                accO[nt] = mfma_f16(bh, f.qd[ks], accO[nt]);
 #if KDA_SPLIT_X
+                const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
                 accX[nt] = mfma_f16(f.kd[ks], bl, accX[nt]);
-#endif
-#if KDA_SPLIT_OI
-                accO[nt] = mfma_f16(bl, f.qd[ks], accO[nt]);
 #endif
             }
             // V of tokens tb + 4lq .. +3 at this lane's column
@@ -1018,20 +1089,8 @@ __global__ __launch_bounds__(NTHR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanP
                     Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bl, Macc[rt][nt]);
 #endif
                 }
-                // O^T += U^T Mqk^T (Mqk strictly lower)
-                accO[nt] = mfma_f16(bh, f.mq[ks], accO[nt]);
-#if KDA_SPLIT_UO
-                accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
-#endif
                 if (nt == 0 && ks == 0) issue_at(nj, nf, M0);
             }
-            // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3; one vector
-            // store (rows past the end are dropped)
-            const f32x4 uf = *reinterpret_cast<const f32x4 *>(sUf + (tb + l16) * TV + 16 * nt + 4 * lq);
-            const float dt = sDG[bsel * (C + D) + tb + l16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) accO[nt][i] += dt * uf[i];
-            buf_st4<TO>(ro, o_off + 16 * nt * (int)sizeof(TO), accO[nt]);
         }
         if (float *sp = p.snap.slot(n, h, H, j + 1, end - start, C, D * D)) {   // uniform across the workgroup
 #pragma unroll
@@ -1158,9 +1217,9 @@ hipError_t run(const PrefillArgs &a) {
         ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc,
                       SnapView{a.snaps, a.snap_every, a.max_snaps}};
         if (wide)
-            hipLaunchKernelGGL((chunk_scan_kernel<32, TO>), dim3(blocks), dim3(NTHR), ScanLds<32>::SIZE, a.stream, sp);
+            hipLaunchKernelGGL((chunk_scan_kernel<32, TO>), dim3(blocks), dim3(SCAN_THR), ScanLds<32>::SIZE, a.stream, sp);
         else
-            hipLaunchKernelGGL((chunk_scan_kernel<16, TO>), dim3(blocks), dim3(NTHR), ScanLds<16>::SIZE, a.stream, sp);
+            hipLaunchKernelGGL((chunk_scan_kernel<16, TO>), dim3(blocks), dim3(SCAN_THR), ScanLds<16>::SIZE, a.stream, sp);
         return hipGetLastError();
     }
 }
