@@ -845,8 +845,10 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
             const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D,
                                      ((Lc - 1) * H * D + D) * (int)sizeof(TO));
             const int bsel = j & 1;
+            __syncthreads();     // Y = V - Kd M is in LDS
             // O^T = M^T Qd^T from the state at the chunk start (published before the
-            // barrier that ended the previous step)
+            // barrier that ended the previous step, replaced only after the next
+            // one), while the recurrence forms U
             f32x4 accO[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -861,7 +863,6 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
 #endif
                 }
             }
-            __syncthreads();     // Y = V - Kd M is in LDS
             __syncthreads();     // U is in LDS
             const float dt = sDG[bsel * (C + D) + tb + l16];
 #pragma unroll
