@@ -818,6 +818,8 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
     const int nch = (end - start + C - 1) / C, c0 = p.sv.first_chunk(n);
     const size_t st_off = ((size_t)n * H + h) * D * D;
     const int tb = 16 * (wave & 3);
+    // bytes from a chunk's first row to the end of its last valid row
+    auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
 
     if (wave >= 4) {
         // Output wavefronts: o = Qd M + Mqk U + d U for token tile tb, from the
@@ -828,22 +830,60 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
         // chunk).
         struct OFrags {
             f16x8 qd[4], mq[2];
+            // 16-byte pieces of the chunk's V tile and of its d and gamma (adjacent
+            // in the record, 192 floats), staged through LDS one chunk ahead for
+            // the whole workgroup (stid: thread index in this group). TV = 16: one
+            // piece, wavefronts 4-5 V (token stid >> 1, columns 8 (stid & 1) ..
+            // +7), 6-7 d and gamma (floats 4 (stid - 128) .. +3; lanes past them
+            // repeat the last piece). TV = 32: piece 0 V (token stid >> 2, columns
+            // 8 (stid & 3) .. +7), piece 1 d and gamma (floats 4 stid .. +3,
+            // repeated past them).
+            u32x4 x[XP];
+        };
+        const int stid = tid - NTHR;
+        const bool x_is_v = TV == 32 || wave < 6;                  // uniform (piece 0)
+        static_assert(Rec::GAM == Rec::DG + C * 4, "d and gamma adjacent in the record");
+        constexpr int VL = TV / 8;                                 // lanes per V row
+        int x_off[XP];
+        x_off[0] = x_is_v ? ((stid / VL) * H * D + col0 + 8 * (stid % VL)) * 2
+                          : Rec::DG + 16 * min(stid - 128, (C + D) / 4 - 1);
+        if constexpr (XP == 2) x_off[XP - 1] = Rec::DG + 16 * min(stid, (C + D) / 4 - 1);
+        // the V / gamma piece of chunk j into LDS buffer j & 1 (read during step j)
+        auto stage = [&](const OFrags &f, int j) {
+            const int bsel = j & 1;
+            if (x_is_v) {
+                // transposed into [col][token]: one column of eight per 16-bit store
+                bf16_t *dst = sV + bsel * TV * SVT + (8 * (stid % VL)) * SVT + (stid / VL);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    dst[e * SVT] = static_cast<bf16_t>(e & 1 ? f.x[0][e >> 1] >> 16 : f.x[0][e >> 1] & 0xffffu);
+            }
+            const int dl = XP == 2 ? stid : stid - 128;            // lane's d / gamma piece
+            if ((XP == 2 || !x_is_v) && dl < (C + D) / 4)
+                *reinterpret_cast<u32x4 *>(sDG + bsel * (C + D) + 4 * dl) = f.x[XP - 1];
         };
         const int r_frag = (wave & 3) * Rec::WAVE + lane * 16;
         // this lane's output: token tb + l16, columns col0 + 4lq .. +3 (O is formed transposed)
         const int o_off = ((tb + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
         auto oissue = [&](int j, OFrags &f) {
             const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
+            const int tok0 = start + j * C, Lc = min(C, end - tok0);
+            // V rows past the end of the sequence read 0 (outside the range): their
+            // values never matter, because beta = 0 there makes the matching columns
+            // of IB zero
+            const auto rv = buf_rsrc(p.v + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, 2));
+#pragma unroll
+            for (int pc = 0; pc < XP; ++pc) f.x[pc] = buf_ld16<u32x4>(pc == 0 && x_is_v ? rv : rr, x_off[pc], 0);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) f.mq[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + ks * 1024);
         };
-        auto ostep = [&](const OFrags &f, int j, OFrags &nf, int nj) {
+        auto ostep = [&](const OFrags &f, int j, const OFrags &f1, OFrags &nf, int nj) {
             oissue(nj, nf);
+            stage(f1, j + 1);    // read by the recurrence in the next step
             const int tok0 = start + j * C, Lc = min(C, end - tok0);
-            const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D,
-                                     ((Lc - 1) * H * D + D) * (int)sizeof(TO));
+            const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, sizeof(TO)));
             const int bsel = j & 1;
             __syncthreads();     // Y = V - Kd M is in LDS
             // O^T = M^T Qd^T from the state at the chunk start (published before the
@@ -891,13 +931,14 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
             OFrags A, B, Cb;
             oissue(0, A);
             oissue(min(1, last), B);
-            __syncthreads();     // the initial state is in LDS
+            stage(A, 0);
+            __syncthreads();     // the initial state and chunk 0's V / gamma are in LDS
             for (int j = 0; j < nch; j += 3) {
-                ostep(A, j, Cb, min(j + 2, last));
+                ostep(A, j, B, Cb, min(j + 2, last));
                 if (j + 1 >= nch) break;
-                ostep(B, j + 1, A, min(j + 3, last));
+                ostep(B, j + 1, Cb, A, min(j + 3, last));
                 if (j + 2 >= nch) break;
-                ostep(Cb, j + 2, B, min(j + 4, last));
+                ostep(Cb, j + 2, A, B, min(j + 4, last));
             }
         }
         return;
@@ -932,49 +973,26 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
     // operands of one chunk, loaded two chunks ahead
     struct Frags {
         f16x8 kd[4], ib[2], kr[2][2];
-        // 16-byte pieces of the chunk's V tile and of its d and gamma (adjacent in
-        // the record, 192 floats), staged through LDS one chunk ahead. TV = 16:
-        // one piece, waves 0-1 V (token tid >> 1, columns 8 (tid & 1) .. +7), waves
-        // 2-3 d and gamma (floats 4 (tid - 128) .. +3; lanes past them repeat the
-        // last piece). TV = 32: piece 0 V (token tid >> 2, columns 8 (tid & 3) ..
-        // +7), piece 1 d and gamma (floats 4 tid .. +3, repeated past them).
-        u32x4 x[XP];
     };
     // loop-invariant byte offsets of this lane's record fragments
     const int r_frag = wave * Rec::WAVE + lane * 16;
-    const bool x_is_v = TV == 32 || wave < 2;                      // uniform (piece 0)
-    static_assert(Rec::GAM == Rec::DG + C * 4, "d and gamma adjacent in the record");
-    constexpr int VL = TV / 8;                                     // lanes per V row
-    int x_off[XP];
-    x_off[0] = x_is_v ? ((tid / VL) * H * D + col0 + 8 * (tid % VL)) * 2
-                      : Rec::DG + 16 * min(tid - 128, (C + D) / 4 - 1);
-    if constexpr (XP == 2) x_off[XP - 1] = Rec::DG + 16 * min(tid, (C + D) / 4 - 1);
-    // bytes from a chunk's first row to the end of its last valid row
-    auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
 
     // The loads of one chunk's operands, as NLD slots in the order they are
-    // consumed: Kd by k-step, the V / gamma piece, IB, Kr. issue()
-    // sends slots [s0, s1); the step spreads them over its phases, so that no
-    // wave stalls on a full vector-memory queue with work of its own waiting.
-    constexpr int NLD = 10 + XP;
+    // consumed: Kd by k-step, IB, Kr. issue() sends slots [s0, s1); the step
+    // spreads them over its phases, so that no wave stalls on a full
+    // vector-memory queue with work of its own waiting.
+    constexpr int NLD = 10;
     auto issue = [&](int j, Frags &f, int s0, int s1) {
         const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
-        const int tok0 = start + j * C, Lc = min(C, end - tok0);
-        // V rows past the end of the sequence read 0 (outside the range): their values
-        // never matter, because beta = 0 there makes the matching columns of IB zero
-        const auto rv = buf_rsrc(p.v + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, 2));
 #pragma unroll
         for (int sl = 0; sl < NLD; ++sl) {
             if (sl < s0 || sl >= s1) continue;
             if (sl < 4) {
                 f.kd[sl] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + sl * 1024);
-            } else if (sl < 4 + XP) {
-                const int pc = sl - 4;
-                f.x[pc] = buf_ld16<u32x4>(pc == 0 && x_is_v ? rv : rr, x_off[pc], 0);
-            } else if (sl < 6 + XP) {
-                f.ib[sl - 4 - XP] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 4 - XP) * 1024);
+            } else if (sl < 6) {
+                f.ib[sl - 4] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 4) * 1024);
             } else {
-                const int e = sl - 6 - XP;
+                const int e = sl - 6;
                 f.kr[e >> 1][e & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + e * 1024);
             }
             // keep the slot order: the in-order vmcnt then lets each use wait
@@ -982,35 +1000,20 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
             __builtin_amdgcn_sched_barrier(0x048F);
         }
     };
-    // where a step issues the next operands: Kd and the V / gamma piece before its
-    // first product (START), IB after the first k-step of U (U0), Kr after the
-    // first k-step of the state update (M0)
+    // where a step issues the next operands: Kd before its first product (START),
+    // IB after the first k-step of U (U0), Kr after the first k-step of the state
+    // update (M0)
     enum { START, U0, M0 };
     auto issue_at = [&](int nj, Frags &nf, int point) {
-        const int a = point == START ? 0 : point == U0 ? 4 + XP : 6 + XP;
-        const int b = point == START ? 4 + XP : point == U0 ? 6 + XP : NLD;
+        const int a = point == START ? 0 : point == U0 ? 4 : 6;
+        const int b = point == START ? 4 : point == U0 ? 6 : NLD;
         issue(nj, nf, a, b);
         // the loads stay where they are issued; compute and LDS traffic may cross
         __builtin_amdgcn_sched_barrier(0x048F);
     };
-    // the V / gamma piece of chunk j into LDS buffer j & 1 (read during step j)
-    auto stage = [&](const Frags &f, int j) {
-        const int bsel = j & 1;
-        if (x_is_v) {
-            // transposed into [col][token]: one column of eight per 16-bit store
-            bf16_t *dst = sV + bsel * TV * SVT + (8 * (tid % VL)) * SVT + (tid / VL);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                dst[e * SVT] = static_cast<bf16_t>(e & 1 ? f.x[0][e >> 1] >> 16 : f.x[0][e >> 1] & 0xffffu);
-        }
-        const int dl = XP == 2 ? tid : tid - 128;                  // lane's d / gamma piece
-        if ((XP == 2 || !x_is_v) && dl < (C + D) / 4)
-            *reinterpret_cast<u32x4 *>(sDG + bsel * (C + D) + 4 * dl) = f.x[XP - 1];
-    };
-
     // Three operand buffers, used round-robin without copies: the loads for a chunk
-    // are issued two chunks before it is consumed, and its V / gamma piece is put
-    // in LDS during the step before.
+    // are issued two chunks before it is consumed (its V tile, d and gamma are put
+    // in LDS by the output wavefronts during the step before).
     auto step = [&](const Frags &f, int j, const Frags &f1, Frags &nf, int nj) {
         issue_at(nj, nf, START);
         const int bsel = j & 1;
@@ -1044,7 +1047,6 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
             *reinterpret_cast<f16x4 *>(sYl + col * SYU + t) = lo;
         }
         __syncthreads();
-        stage(f1, j + 1);
         // U = IB Y (Y split hi + lo)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -1116,7 +1118,6 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
         const int last = nch - 1;
         issue(0, A, 0, NLD);
         issue(min(1, last), B, 0, NLD);
-        stage(A, 0);
         __syncthreads();
         for (int j = 0; j < nch; j += 3) {
             step(A, j, B, Cb, min(j + 2, last));
