@@ -756,8 +756,7 @@ struct ScanLds {
     static constexpr int U = Y + 2 * TV * SYU * 2;   // fp16 [2][TV][SYU] U hi / lo, [col][token]
     static constexpr int V = U + 2 * TV * SYU * 2;   // bf16 [2][TV][SVT] V of a chunk, [col][token], double-buffered
     static constexpr int DG = V + 2 * TV * SVT * 2;  // fp32 [2][C + D] d then gamma of a chunk, double-buffered
-    static constexpr int UF = DG + 2 * (C + D) * 4;  // fp32 [C][TV] U, [token][col]
-    static constexpr int SIZE = UF + C * TV * 4;
+    static constexpr int SIZE = DG + 2 * (C + D) * 4;
 };
 
 struct ScanParams {
@@ -801,7 +800,6 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
     _Float16 *sUl = sUh + TV * SYU;
     bf16_t *sV = reinterpret_cast<bf16_t *>(smem + Lo::V);
     float *sDG = reinterpret_cast<float *>(smem + Lo::DG);
-    float *sUf = reinterpret_cast<float *>(smem + Lo::UF);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
@@ -917,11 +915,14 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
                     accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
 #endif
                 }
-                // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3; one vector
-                // store (rows past the end are dropped)
-                const f32x4 uf = *reinterpret_cast<const f32x4 *>(sUf + (tb + l16) * TV + 16 * nt + 4 * lq);
+                // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3, with U as its
+                // hi + lo parts (U to 2^-22 relative); one vector store (rows past
+                // the end are dropped)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) accO[nt][i] += dt * uf[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int at = (16 * nt + 4 * lq + i) * SYU + tb + l16;
+                    accO[nt][i] += dt * (static_cast<float>(sUh[at]) + static_cast<float>(sUl[at]));
+                }
                 buf_st4<TO>(ro, o_off + 16 * nt * (int)sizeof(TO), accO[nt]);
             }
             __syncthreads();     // the next state is in LDS
@@ -1063,10 +1064,7 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
             }
             f16x4 hi, lo;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                SPLITH(u[i], hi[i], lo[i]);
-                sUf[(tb + 4 * lq + i) * TV + 16 * nt + l16] = u[i];    // fp32 U for d U in the output
-            }
+            for (int i = 0; i < 4; ++i) SPLITH(u[i], hi[i], lo[i]);
             const int col = 16 * nt + l16, t = tb + 4 * lq;
             *reinterpret_cast<f16x4 *>(sUh + col * SYU + t) = hi;
             *reinterpret_cast<f16x4 *>(sUl + col * SYU + t) = lo;
