@@ -13,16 +13,20 @@
 //     O     = Qd M + Mqk U
 //     M_out = Diag(gamma) M + Kr^T U
 //
-// prep  (one workgroup per (chunk, head), all chunks in parallel): decays
-//       as products of alpha = exp(g) inside 16-token blocks, L and Mqk on
-//       bf16 MFMA with hi/lo split operands, the unit-lower-triangular
-//       inverse by blocked substitution (fp32 MFMA off the diagonal), and a
-//       record of the scan's left operands in fp16, laid out as MFMA
-//       fragments so that the scan loads them with 16-byte coalesced reads.
-// scan  (one workgroup per (sequence, head, 16-column value tile), its chunks
-//       in order): the fp32 state tile stays in registers; five fp16 MFMA
-//       contractions per chunk with the right operand (state, V - Kd M, U)
-//       split into fp16 hi + lo and fp32 accumulation.
+// prep  (persistent, one workgroup per CU walking the (chunk, head) items,
+//       all chunks in parallel): decays as products of alpha = exp(g) inside
+//       16-token blocks; L and Mqk with the diagonal 16x16 blocks on fp32
+//       MFMA and the off-diagonal ones on fp16 MFMA (every factor <= 1 there);
+//       the unit-lower-triangular inverse by substitution on the diagonal
+//       blocks and fp32 MFMA products off it; and a record of the scan's
+//       operands in fp16, laid out as MFMA fragments so that the scan loads
+//       them with 16-byte coalesced reads.
+// scan  (one workgroup per (sequence, head, 16- or 32-column value tile), its
+//       chunks in order): four recurrence wavefronts keep the fp32 state tile
+//       in registers and form X = Kd M, U = IB (V - X) and the state update on
+//       fp16 MFMA with the right operand (state, V - X, U) split into fp16
+//       hi + lo and fp32 accumulation; four output wavefronts form o from the
+//       state and U the recurrence shares in LDS.
 //
 // Every decay factor that is formed is <= 1, except on the diagonal 16x16
 // blocks of L and Mqk, which use the block's own start as reference: their
