@@ -55,13 +55,17 @@ constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 
 // Which right-hand operands of the scan's fp16 contractions are split into
 // hi + lo (two MFMAs) rather than rounded once. The state update keeps ~22
-// bits in every operand that feeds back into the state (X, V - X, U); the
-// output-only products round once (11 bits).
+// bits in every operand that feeds back into the state (X, V - X, U). The
+// output-only products (formed by the output wavefronts) are split too on
+// 16-column tiles, where those wavefronts have the time (measured slightly
+// faster, o error 2.5e-3 -> 1.4e-3 x RMS on the 8k workload), and round once
+// (11 bits) on 32-column tiles, where splitting them lengthened the step;
+// KDA_SPLIT_OI / KDA_SPLIT_UO = 1 split them on both.
 #ifndef KDA_SPLIT_X
 #define KDA_SPLIT_X 1     // the state in X = Kd M
 #endif
 #ifndef KDA_SPLIT_OI
-#define KDA_SPLIT_OI 0    // the state in O = Qd M (o only: its error is not fed back)
+#define KDA_SPLIT_OI 0    // the state in O = Qd M on 32-column tiles (o only: its error is not fed back)
 #endif
 #ifndef KDA_SPLIT_Y
 #define KDA_SPLIT_Y 1     // V - X in U = IB (V - X)
@@ -76,7 +80,7 @@ constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 #define KDA_SCAN_BUFS 3   // scan operand buffers in rotation (loads two chunks ahead)
 #endif
 #ifndef KDA_SPLIT_UO
-#define KDA_SPLIT_UO 0    // U in O += Mqk U (o only)
+#define KDA_SPLIT_UO 0    // U in O += Mqk U on 32-column tiles (o only)
 #endif
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -899,10 +903,10 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
                 for (int ks = 0; ks < 4; ++ks) {
                     const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
                     accO[nt] = mfma_f16(bh, f.qd[ks], accO[nt]);
-#if KDA_SPLIT_OI
-                    const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
-                    accO[nt] = mfma_f16(bl, f.qd[ks], accO[nt]);
-#endif
+                    if constexpr (KDA_SPLIT_OI || TV == 16) {
+                        const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
+                        accO[nt] = mfma_f16(bl, f.qd[ks], accO[nt]);
+                    }
                 }
             }
             __syncthreads();     // U is in LDS
@@ -914,10 +918,10 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(S
                     // O^T += U^T Mqk^T (Mqk strictly lower)
                     const f16x8 bh = lds8h(sUh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
                     accO[nt] = mfma_f16(bh, f.mq[ks], accO[nt]);
-#if KDA_SPLIT_UO
-                    const f16x8 bl = lds8h(sUl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-                    accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
-#endif
+                    if constexpr (KDA_SPLIT_UO || TV == 16) {
+                        const f16x8 bl = lds8h(sUl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
+                        accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
+                    }
                 }
                 // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3, with U as its
                 // hi + lo parts (U to 2^-22 relative); one vector store (rows past
