@@ -73,8 +73,8 @@ constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 #ifndef KDA_SPLIT_U
 #define KDA_SPLIT_U 1     // U in M += Kr^T U
 #endif
-#ifndef KDA_SCAN_MIN_WG
-#define KDA_SCAN_MIN_WG 1  // scan workgroups that must fit on one CU (2: registers capped at 256 per lane)
+#ifndef KDA_SCAN_MIN_WAVES
+#define KDA_SCAN_MIN_WAVES 1  // scan waves per SIMD its registers must allow (4: two workgroups per CU, 128 registers)
 #endif
 #ifndef KDA_SCAN_BUFS
 #define KDA_SCAN_BUFS 3   // scan operand buffers in rotation (loads two chunks ahead)
@@ -793,7 +793,7 @@ template <> __device__ __forceinline__ void buf_st4<bf16_t>(__amdgpu_buffer_rsrc
 }
 
 template <int TV, typename TO>
-__global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WG) void chunk_scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WAVES) void chunk_scan_kernel(ScanParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = ScanLds<TV>;
     constexpr int NT = TV / 16;
