@@ -112,16 +112,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, co
     }
 }
 
-#ifndef KDA_DECODE_NT
-#define KDA_DECODE_NT 128
-#endif
-#ifndef KDA_DECODE_WDIV
-#define KDA_DECODE_WDIV 2
-#endif
-
+// 128 threads per workgroup, each workgroup one half (64 value columns) of a
+// chain's state: two workgroups per (sequence, head)
 template <int D, typename TI, typename TB, typename TO>
 hipError_t launch_t(const DecodeArgs &a) {
-    constexpr int NT = KDA_DECODE_NT, W = D / KDA_DECODE_WDIV;
+    constexpr int NT = 128, W = D / 2;
     const unsigned chains = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
     hipLaunchKernelGGL((decode_kernel<D, NT, W, TI, TB, TO>), dim3(chains * (D / W)), dim3(NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),

@@ -1152,18 +1152,16 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WAVES) void chunk_scan_kerne
 }
 
 // ---------------------------------------------------------------- host
-// persistent prep: one workgroup per compute unit (its LDS use allows one)
-long long prep_grid() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
+// Compute units of the device the launch goes to (the caller's current
+// device). Queried on every call: the library keeps no per-process cache, so
+// concurrent first calls and several devices need no synchronisation.
+hipError_t device_cus(int *cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && *cus < 1) e = hipErrorInvalidDevice;
+    return e;
 }
 
 // workspace: chunk offsets (N + 1 int32), the chunk table (maxc int2), records
@@ -1179,6 +1177,8 @@ hipError_t run(const PrefillArgs &a) {
     char *recs = ws + ws_offs(a.N) + ws_meta(maxc);
     SeqView sv{a.cu_seqlens, chunk_off, a.N, a.T, C};
     const bool varlen = a.cu_seqlens != nullptr;
+    int cus = 0;
+    if (const hipError_t e = device_cus(&cus); e != hipSuccess) return e;
     if (varlen) {
         hipError_t e = launch_chunk_plan(a.cu_seqlens, a.N, C, chunk_off, a.stream);
         if (e != hipSuccess) return e;
@@ -1190,27 +1190,24 @@ hipError_t run(const PrefillArgs &a) {
     {
         // kernel variant [varlen][per-head gate][L2-normalised q, k]
         using Kern = void (*)(PrepParams);
-        static const Kern kerns[2][2][2] = {
+        const Kern kerns[2][2][2] = {
             {{chunk_prep_kernel<TB, false, false, false>, chunk_prep_kernel<TB, false, false, true>},
              {chunk_prep_kernel<TB, false, true, false>, chunk_prep_kernel<TB, false, true, true>}},
             {{chunk_prep_kernel<TB, true, false, false>, chunk_prep_kernel<TB, true, false, true>},
              {chunk_prep_kernel<TB, true, true, false>, chunk_prep_kernel<TB, true, true, true>}}};
-        static bool attr[2][2][2] = {};
         const Kern kern = kerns[varlen][a.g_head][a.qk_norm];
-        if (!attr[varlen][a.g_head][a.qk_norm]) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
-            if (e != hipSuccess) return e;
-            attr[varlen][a.g_head][a.qk_norm] = true;
-        }
+        // set on every call (idempotent; no process-wide "already set" flag to race on)
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
+        if (e != hipSuccess) return e;
         PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, meta,
                       a.H, recs, maxc, a.norm_eps};
         // persistent: one workgroup per CU walks the (chunk, head) items
         const long long items = maxc * a.H;
-        const unsigned grid = (unsigned)std::min<long long>(items, prep_grid());
+        const unsigned grid = (unsigned)std::min<long long>(items, cus);
         if (items > 0) {
             hipLaunchKernelGGL(kern, dim3(grid), dim3(PTHR), PrepLds::SIZE, a.stream, pp);
-            const hipError_t e = hipGetLastError();
+            e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }
@@ -1219,7 +1216,7 @@ hipError_t run(const PrefillArgs &a) {
         // fill the CUs four times over or more (many chains, e.g. packed batches):
         // a CU then reads each record once per 32 columns instead of per 16
         const int chains = a.N * a.H;
-        const bool wide = (long long)chains * (D / 16) >= 4 * prep_grid();
+        const bool wide = (long long)chains * (D / 16) >= 4LL * cus;
         const int team = wide ? D / 32 : D / 16;
         const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
         ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc,

@@ -89,10 +89,45 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, device) -> Optional[int]:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+_FLOAT_IO = (torch.float32, torch.bfloat16)
+
+
+def _expect(t, name, shape, dtypes, optional=False):
+    """Raise ValueError unless tensor ``t`` has exactly ``shape`` and a dtype in ``dtypes``."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {[str(d) for d in dtypes]}, got {t.dtype}")
+
+
+def _same_gpu(**tensors) -> torch.device:
+    """Every given tensor is a contiguous GPU tensor on one device; returns that device.
+    Checked after shapes and dtypes, so that those errors are reported on any device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (libkda reads device memory), got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other tensors on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return dev
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -105,6 +140,46 @@ def _dt(t: torch.Tensor) -> int:
 def kda_prefill_workspace_size(N: int, T_total: int, H: int, Dk: int, Dv: int, C: int,
                                io_dtype: torch.dtype) -> int:
     return int(load_library().kda_prefill_workspace_size(N, T_total, H, Dk, Dv, C, _DT[io_dtype]))
+
+
+def _check_prefill(q, k, v, g, beta, S0, out, S_out, cu_seqlens, workspace, g_head, snapshots=None,
+                   max_snapshots=0):
+    """Shapes, dtypes and devices of a prefill call, checked before the library sees a pointer
+    (the C ABI receives raw pointers and cannot tell an int64 cu_seqlens from an int32 one)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, Dk]")
+    B, T, H, Dk = q.shape
+    _expect(q, "q", (B, T, H, Dk), _FLOAT_IO)
+    _expect(k, "k", (B, T, H, Dk), (q.dtype,))
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, H, Dv]")
+    Dv = v.shape[-1]
+    _expect(v, "v", (B, T, H, Dv), (q.dtype,))
+    if g_head:
+        _expect(g, "g", (B, T, H), (torch.float32,), optional=True)
+    else:
+        _expect(g, "g", (B, T, H, Dk), (torch.float32,))
+    _expect(beta, "beta", (B, T, H), _FLOAT_IO)
+    if cu_seqlens is not None:
+        if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 >= 2 offsets")
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError(f"cu_seqlens must be int32, got {cu_seqlens.dtype}")
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _expect(S0, "S0", (N, H, Dk, Dv), (torch.float32,), optional=True)
+    _expect(out, "out", (B, T, H, Dv), _FLOAT_IO, optional=True)
+    _expect(S_out, "S_out", (N, H, Dk, Dv), (torch.float32,), optional=True)
+    if snapshots is not None:
+        _expect(snapshots, "snapshots", (N, H, max_snapshots, Dk, Dv), (torch.float32,))
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.dim() != 1 or
+                                  workspace.dtype != torch.uint8):
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    return _same_gpu(q=q, k=k, v=v, g=g, beta=beta, S0=S0, out=out, S_out=S_out, cu_seqlens=cu_seqlens,
+                     snapshots=snapshots, workspace=workspace)
 
 
 def _prefill_buffers(lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state):
@@ -125,17 +200,19 @@ def _prefill_buffers(lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, work
 def _prefill(entry, q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace, stream,
              return_state, qk_l2norm=False, l2norm_eps=1e-6):
     lib = load_library()
-    (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
-        lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_out),
-            _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta), _dt(out))
-    if qk_l2norm:
-        opt = Options(gate=GATE_HEAD if entry == "gdn_prefill" else GATE_CHANNEL, qk_l2norm=1,
-                      l2norm_eps=l2norm_eps)
-        entry = "kda_prefill_ex"
-        st = lib.kda_prefill_ex(*args, ctypes.byref(opt), _ptr(workspace), ws_bytes, _stream(stream))
-    else:
-        st = getattr(lib, entry)(*args, _ptr(workspace), ws_bytes, _stream(stream))
+    dev = _check_prefill(q, k, v, g, beta, S0, out, S_out, cu_seqlens, workspace, entry == "gdn_prefill")
+    with torch.cuda.device(dev):
+        (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
+            lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out), _ptr(S_out),
+                _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta), _dt(out))
+        if qk_l2norm:
+            opt = Options(gate=GATE_HEAD if entry == "gdn_prefill" else GATE_CHANNEL, qk_l2norm=1,
+                          l2norm_eps=l2norm_eps)
+            entry = "kda_prefill_ex"
+            st = lib.kda_prefill_ex(*args, ctypes.byref(opt), _ptr(workspace), ws_bytes, _stream(stream, dev))
+        else:
+            st = getattr(lib, entry)(*args, _ptr(workspace), ws_bytes, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, entry)
     return out, S_out
@@ -170,15 +247,21 @@ def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max
     each sequence into ``snapshots`` [N, H, max_snapshots, Dk, Dv] fp32 (slots past a
     sequence's end are not written). Returns (out, S_out, snapshots)."""
     lib = load_library()
-    (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
-        lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
     if snapshots is None:
-        snapshots = torch.full((N, H, max_snapshots, Dk, Dv), float("nan"), dtype=torch.float32,
-                               device=q.device)
-    st = lib.kda_prefill_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
-                                   _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q),
-                                   _dt(beta), _dt(out), snapshot_every, max_snapshots, _ptr(snapshots),
-                                   _ptr(workspace), ws_bytes, _stream(stream))
+        if not isinstance(q, torch.Tensor) or q.dim() != 4 or not isinstance(v, torch.Tensor) or v.dim() != 4:
+            raise ValueError("q must be [B, T, H, Dk] and v [B, T, H, Dv]")
+        N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        snapshots = torch.full((N, q.shape[2], max_snapshots, q.shape[3], v.shape[3]), float("nan"),
+                               dtype=torch.float32, device=q.device)
+    dev = _check_prefill(q, k, v, g, beta, S0, out, S_out, cu_seqlens, workspace, False, snapshots,
+                         max_snapshots)
+    with torch.cuda.device(dev):
+        (B, T, H, Dk, Dv, N), out, S_out, workspace, ws_bytes = _prefill_buffers(
+            lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, workspace, return_state)
+        st = lib.kda_prefill_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
+                                       _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q),
+                                       _dt(beta), _dt(out), snapshot_every, max_snapshots, _ptr(snapshots),
+                                       _ptr(workspace), ws_bytes, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_snapshots")
     return out, S_out, snapshots
@@ -186,19 +269,33 @@ def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max
 
 def _decode(entry, q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm=False, l2norm_eps=1e-6):
     lib = load_library()
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not isinstance(v, torch.Tensor) or v.dim() != 3:
+        raise ValueError("q must be [N, H, Dk] and v [N, H, Dv]")
     N, H, Dk = q.shape
     Dv = v.shape[-1]
+    _expect(q, "q", (N, H, Dk), _FLOAT_IO)
+    _expect(k, "k", (N, H, Dk), (q.dtype,))
+    _expect(v, "v", (N, H, Dv), (q.dtype,))
+    if entry == "gdn_decode":
+        _expect(g, "g", (N, H), (torch.float32,), optional=True)
+    else:
+        _expect(g, "g", (N, H, Dk), (torch.float32,))
+    _expect(beta, "beta", (N, H), _FLOAT_IO)
+    _expect(S, "S", (N, H, Dk, Dv), (torch.float32,))
+    _expect(out, "out", (N, H, Dv), _FLOAT_IO, optional=True)
+    dev = _same_gpu(q=q, k=k, v=v, g=g, beta=beta, S=S, out=out)
     if out is None:
         out = torch.empty(N, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out), N, H, Dk, Dv, _dt(q),
             _dt(beta), _dt(out))
-    if qk_l2norm:
-        opt = Options(gate=GATE_HEAD if entry == "gdn_decode" else GATE_CHANNEL, qk_l2norm=1,
-                      l2norm_eps=l2norm_eps)
-        entry = "kda_decode_ex"
-        st = lib.kda_decode_ex(*args, ctypes.byref(opt), _stream(stream))
-    else:
-        st = getattr(lib, entry)(*args, _stream(stream))
+    with torch.cuda.device(dev):
+        if qk_l2norm:
+            opt = Options(gate=GATE_HEAD if entry == "gdn_decode" else GATE_CHANNEL, qk_l2norm=1,
+                          l2norm_eps=l2norm_eps)
+            entry = "kda_decode_ex"
+            st = lib.kda_decode_ex(*args, ctypes.byref(opt), _stream(stream, dev))
+        else:
+            st = getattr(lib, entry)(*args, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, entry)
     return out
@@ -225,16 +322,20 @@ def kda_output_gate(o, gate, weight=None, *, eps: float = 1e-6, out=None,
     o, gate: [..., H, Dv] (same shape); weight: [Dv] fp32 or None (ones).
     ``out`` may be ``o`` itself when the dtypes match. Returns out."""
     lib = load_library()
-    if gate.shape != o.shape:
-        raise ValueError("gate must have the shape of o")
+    if not isinstance(o, torch.Tensor) or o.dim() < 2:
+        raise ValueError("o must be a tensor [..., H, Dv]")
+    _expect(o, "o", o.shape, _FLOAT_IO)
+    _expect(gate, "gate", o.shape, _FLOAT_IO)
     H, Dv = o.shape[-2], o.shape[-1]
     rows = o.numel() // (H * Dv) if o.numel() else 0
-    if weight is not None and (weight.dtype != torch.float32 or weight.numel() != Dv):
-        raise ValueError("weight must be a float32 tensor of Dv elements")
+    _expect(weight, "weight", (Dv,), (torch.float32,), optional=True)
+    _expect(out, "out", o.shape, _FLOAT_IO, optional=True)
+    dev = _same_gpu(o=o, gate=gate, weight=weight, out=out)
     if out is None:
         out = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=o.device)
-    st = lib.kda_output_gate(_ptr(o), _ptr(gate), _ptr(weight), _ptr(out), rows, H, Dv, float(eps),
-                             _dt(o), _dt(gate), _dt(out), _stream(stream))
+    with torch.cuda.device(dev):
+        st = lib.kda_output_gate(_ptr(o), _ptr(gate), _ptr(weight), _ptr(out), rows, H, Dv, float(eps),
+                                 _dt(o), _dt(gate), _dt(out), _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_output_gate")
     return out

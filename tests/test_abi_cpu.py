@@ -236,3 +236,25 @@ def _output_gate(lib, **kw):
 ])
 def test_output_gate_argument_errors(lib, kw, status):
     assert _output_gate(lib, **kw) == status
+
+
+def test_host_paths_from_several_threads(lib):
+    """The host side (argument checks, workspace sizing) is a pure function of its
+    arguments: the same answers from 8 threads at once."""
+    import threading
+    want_ws = lib.kda_prefill_workspace_size(3, 1000, 4, 128, 128, 64, 1)
+    want_err = _prefill(lib, N=0)
+    bad = []
+
+    def work():
+        for _ in range(2000):
+            if lib.kda_prefill_workspace_size(3, 1000, 4, 128, 128, 64, 1) != want_ws or \
+                    _prefill(lib, N=0) != want_err:
+                bad.append(1)
+
+    ts = [threading.Thread(target=work) for _ in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert want_ws > 0 and want_err == -1 and not bad
