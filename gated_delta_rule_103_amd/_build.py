@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_abi.cpp", "decode.hip", "prefill_f32.hip", "prefill_mfma.hip", "output_gate.hip"]
+SOURCES = ["kda_abi.cpp", "decode.hip", "prefill_f32.hip", "prefill_mfma.hip", "output_gate.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -65,7 +65,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
                  int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
                  int snapshot_every, int max_snapshots, float *snapshots, void *workspace,
                  size_t workspace_bytes, void *stream, bool g_head = false, bool qk_norm = false,
-                 float norm_eps = 0.f) {
+                 float norm_eps = 0.f, bool noalloc = false) {
     // a per-head gate may be absent (no decay); a per-channel gate may not
     if (!q || !k || !v || (!g && !g_head) || !beta || !out) return KDA_ERR_INVALID_ARG;
     if (N < 1 || B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1 || C < 1) return KDA_ERR_INVALID_ARG;
@@ -88,6 +88,12 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     if (io_dtype == KDA_F32 && (beta_dtype != KDA_F32 || out_dtype != KDA_F32)) return KDA_ERR_UNSUPPORTED;
     if (snapshots && snapshot_every % C != 0) return KDA_ERR_UNSUPPORTED;
     const size_t need = workspace_for(N, T_total, H, Dk, Dv, C, io_dtype);
+    if (noalloc) {
+        // the library's fixed per-device array serves as the workspace
+        if (need > kda::kNoAllocScratchBytes) return KDA_ERR_WORKSPACE;
+        if (kda::noalloc_scratch(&workspace) != hipSuccess) return KDA_ERR_HIP;
+        workspace_bytes = kda::kNoAllocScratchBytes;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return KDA_ERR_WORKSPACE;
 
@@ -120,6 +126,17 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g, con
                 kda_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(q, k, v, g, beta, S0, out, S_out, cu_seqlens, N, B, T, H, Dk, Dv, C, io_dtype,
                         beta_dtype, out_dtype, 0, 0, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kda_prefill_noalloc(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                        const float *S0, void *out, float *S_out, const int32_t *cu_seqlens, int N, int B,
+                        int T, int H, int Dk, int Dv, int C, kda_dtype io_dtype, kda_dtype beta_dtype,
+                        kda_dtype out_dtype, void *stream) {
+    // every argument is checked first, then the workspace size against the
+    // fixed array, and only then is the array's address on the current device
+    // taken: no allocation
+    return prefill_impl(q, k, v, g, beta, S0, out, S_out, cu_seqlens, N, B, T, H, Dk, Dv, C, io_dtype,
+                        beta_dtype, out_dtype, 0, 0, nullptr, nullptr, 0, stream, false, false, 0.f, true);
 }
 
 int kda_prefill_snapshots(const void *q, const void *k, const void *v, const float *g, const void *beta,

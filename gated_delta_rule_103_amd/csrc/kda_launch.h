@@ -77,6 +77,11 @@ hipError_t launch_prefill_f32(const PrefillArgs &a);
 size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C);
 hipError_t launch_prefill_mfma(const PrefillArgs &a);
 
+// kda_prefill_noalloc: the size of its fixed device workspace, and the address
+// of that workspace on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // single-token decode.
 hipError_t launch_decode(const DecodeArgs &a);
 

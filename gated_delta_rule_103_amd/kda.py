@@ -60,6 +60,9 @@ def load_library() -> ctypes.CDLL:
     lib.kda_prefill.restype = i
     lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 i, i, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.kda_prefill_noalloc.restype = i
+    lib.kda_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i, i, i, i, i, i, i, i, i, i, vp]
     lib.kda_prefill_snapshots.restype = i
     lib.kda_prefill_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           i, i, i, i, i, i, i, i, i, i, i, i, vp, vp, sz, vp]
@@ -227,6 +230,30 @@ def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=N
     Returns (out [B, T, H, Dv], S_out [N, H, Dk, Dv] or None)."""
     return _prefill("kda_prefill", q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace,
                     stream, return_state, qk_l2norm, l2norm_eps)
+
+
+def kda_prefill_noalloc(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,
+                        out_dtype: Optional[torch.dtype] = None, stream=None, return_state: bool = True):
+    """kda_prefill with the library's fixed per-device workspace (no allocation inside the
+    call; ``out`` and ``S_out`` are allocated here only when not given). Sizes whose
+    workspace exceeds the fixed array raise KDAError(KDA_ERR_WORKSPACE). Calls that
+    overlap in time on one GPU share that array and race."""
+    lib = load_library()
+    dev = _check_prefill(q, k, v, g, beta, S0, out, S_out, cu_seqlens, None, False)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty(B, T, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
+    if S_out is None and return_state:
+        S_out = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
+    with torch.cuda.device(dev):
+        st = lib.kda_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
+                                     _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
+                                     _dt(out), _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_noalloc")
+    return out, S_out
 
 
 def gdn_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=None, C: int = 64,

@@ -24,7 +24,9 @@
  *   - All tensor pointers are DEVICE pointers, dense and contiguous, in the
  *     layouts given below; q, k, v, g and out of kda_prefill must be
  *     16-byte aligned. The caller owns every buffer; the library never allocates or
- *     frees device memory and keeps no mutable global state.
+ *     frees device memory and keeps no mutable global state, with one stated
+ *     exception: kda_prefill_noalloc's fixed per-device workspace. Calls from
+ *     several host threads at once are safe.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream). Nothing is synchronised and no device memory is read on the
  *     host. Kernel faults surface at the caller's next synchronisation.
@@ -144,6 +146,30 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g,
                 const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
                 int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill_noalloc -- kda_prefill without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It calls no allocator.
+ *
+ * All arguments, layouts, the support matrix and the results as for
+ * kda_prefill (the same kernels run). The workspace is instead a fixed array
+ * of KDA_NOALLOC_SCRATCH_BYTES (128 MiB) in the library's device memory, one
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends. Sizes whose workspace (kda_prefill_workspace_size) exceeds it return
+ * KDA_ERR_WORKSPACE before anything is launched. The array is looked up on
+ * the device current at the call, and `stream` must belong to that device.
+ * Every call on one GPU shares the array: calls that overlap in time on the
+ * same GPU (different streams, or host threads without ordering) race and
+ * give undefined results. Calls ordered on one stream are safe; nothing in
+ * the array needs to be cleared between them.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int kda_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                        const void *beta, const float *S0, void *out, float *S_out,
+                        const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                        int C, kda_dtype io_dtype, kda_dtype beta_dtype, kda_dtype out_dtype,
+                        void *stream);
 
 /*
  * kda_prefill_snapshots -- kda_prefill that also saves intermediate states

@@ -258,3 +258,15 @@ def test_host_paths_from_several_threads(lib):
     for t in ts:
         t.join()
     assert want_ws > 0 and want_err == -1 and not bad
+
+
+def test_noalloc_checks_before_touching_the_device(lib):
+    """kda_prefill_noalloc validates every argument, then the workspace size against its
+    fixed array, before it looks the array up on a device (none is needed here)."""
+    fake = ctypes.c_void_p(256)
+    call = lambda **kw: lib.kda_prefill_noalloc(
+        kw.get("q", fake), fake, fake, fake, fake, None, fake, None, None, 1, 1, kw.get("T", 64), 32, 128, 128,
+        kw.get("C", 64), 1, 1, 1, None)
+    assert call(q=None) == -1
+    assert call(C=8) == -2
+    assert call(T=65536) == -3          # 65536 x 32 heads needs ~1.1 GB of records
