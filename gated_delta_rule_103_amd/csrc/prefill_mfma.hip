@@ -7,9 +7,9 @@
 //     Kd = k * exp(a),  Qd = q * exp(a),  Kr = k * exp(a_last - a)
 //     Mqk[t,s] = sum_c q_t k_s exp(a_t - a_s)   (s <= t)
 //     L[t,s]   = beta_t sum_c k_t k_s exp(a_t - a_s)   (s < t)
-//     IB       = (I + L)^{-1} Diag(beta)
+//     IB       = (I + L)^{-1} Diag(beta),   W = IB Kd,   U~ = IB V
 // and per chunk of one (sequence, head), with the state M = S^T:
-//     U     = IB (V - Kd M)
+//     U     = U~ - W M
 //     O     = Qd M + Mqk U
 //     M_out = Diag(gamma) M + Kr^T U
 //
@@ -18,15 +18,16 @@
 //       16-token blocks; L and Mqk with the diagonal 16x16 blocks on fp32
 //       MFMA and the off-diagonal ones on fp16 MFMA (every factor <= 1 there);
 //       the unit-lower-triangular inverse by substitution on the diagonal
-//       blocks and fp32 MFMA products off it; and a record of the scan's
-//       operands in fp16, laid out as MFMA fragments so that the scan loads
-//       them with 16-byte coalesced reads.
-// scan  (one workgroup per (sequence, head, 16- or 32-column value tile), its
-//       chunks in order): four recurrence wavefronts keep the fp32 state tile
-//       in registers and form X = Kd M, U = IB (V - X) and the state update on
-//       fp16 MFMA with the right operand (state, V - X, U) split into fp16
-//       hi + lo and fp32 accumulation; four output wavefronts form o from the
-//       state and U the recurrence shares in LDS.
+//       blocks and fp32 MFMA products off it; W = IB Kd on fp16 MFMA; and a
+//       record of the scan's operands in fp16, laid out as MFMA fragments in
+//       the register order of the scan's accumulators.
+// scan  (one workgroup of four wavefronts per (sequence, head, 16- or
+//       32-column value tile), its chunks in order): each wavefront keeps 32
+//       rows of the fp32 state in registers; per chunk it forms its share of
+//       U (and of Qd M) over those rows, the four shares meet in LDS at the
+//       step's one barrier, and every wavefront then updates its rows and forms
+//       o for its 16 tokens. Contractions on fp16 MFMA with the state and U
+//       split into fp16 hi + lo, fp32 accumulation.
 //
 // Every decay factor that is formed is <= 1, except on the diagonal 16x16
 // blocks of L and Mqk, which use the block's own start as reference: their
@@ -49,43 +50,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;       // Dk == Dv
 constexpr int C = 64;        // chunk length
-constexpr int NTHR = 256;    // scan: 4 recurrence wavefronts, one per SIMD ...
-constexpr int SCAN_THR = 2 * NTHR;   // ... and 4 output wavefronts beside them
 constexpr float kTiny = 1.17549435e-38f;  // FLT_MIN
 
-// Which right-hand operands of the scan's fp16 contractions are split into
-// hi + lo (two MFMAs) rather than rounded once. The state update keeps ~22
-// bits in every operand that feeds back into the state (X, V - X, U). The
-// output-only products (formed by the output wavefronts) are split too on
-// 16-column tiles, where those wavefronts have the time (measured slightly
-// faster, o error 2.5e-3 -> 1.4e-3 x RMS on the 8k workload), and round once
-// (11 bits) on 32-column tiles, where splitting them lengthened the step;
-// KDA_SPLIT_OI / KDA_SPLIT_UO = 1 split them on both.
-#ifndef KDA_SPLIT_X
-#define KDA_SPLIT_X 1     // the state in X = Kd M
-#endif
-#ifndef KDA_SPLIT_OI
-#define KDA_SPLIT_OI 0    // the state in O = Qd M on 32-column tiles (o only: its error is not fed back)
-#endif
-#ifndef KDA_SPLIT_Y
-#define KDA_SPLIT_Y 1     // V - X in U = IB (V - X)
-#endif
-#ifndef KDA_SPLIT_U
-#define KDA_SPLIT_U 1     // U in M += Kr^T U
-#endif
-#ifndef KDA_SCAN_MIN_WAVES
-#define KDA_SCAN_MIN_WAVES 1  // scan waves per SIMD its registers must allow (4: two workgroups per CU, 128 registers)
-#endif
-#ifndef KDA_SCAN_BUFS
-#define KDA_SCAN_BUFS 3   // scan operand buffers in rotation (loads two chunks ahead)
-#endif
-#ifndef KDA_SPLIT_UO
-#define KDA_SPLIT_UO 0    // U in O += Mqk U on 32-column tiles (o only)
-#endif
-
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -107,6 +73,20 @@ template <> __device__ __forceinline__ void buf_st<bf16_t>(__amdgpu_buffer_rsrc_
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)), r, voff, 0, 0);
 }
 
+// four consecutive outputs with one store (16 bytes fp32, 8 bytes bf16)
+template <typename T> __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x);
+template <> __device__ __forceinline__ void buf_st4<float>(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, 0, 0);
+}
+template <> __device__ __forceinline__ void buf_st4<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[0])) |
+                        (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[1]))) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2])) |
+                        (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[3]))) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, voff, 0, 0);
+}
+
 template <typename T> __device__ __forceinline__ float ld_scalar(const T *p, size_t i);
 template <> __device__ __forceinline__ float ld_scalar<float>(const float *p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld_scalar<bf16_t>(const bf16_t *p, size_t i) {
@@ -118,15 +98,8 @@ template <> __device__ __forceinline__ void st_scalar<bf16_t>(bf16_t *p, size_t 
     p[i] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
 }
 
-// x = hi + lo, hi = bf16(x), lo = bf16(x - hi): about 16 significant bits
-#define SPLIT2(x, HI, LO)                                   \
-    do {                                                    \
-        const float x_ = (x);                               \
-        const __bf16 h_ = static_cast<__bf16>(x_);          \
-        (HI) = h_;                                          \
-        (LO) = static_cast<__bf16>(x_ - bf2f(h_));          \
-    } while (0)
-// the same in fp16: about 22 significant bits (|x| < 65504)
+// x = hi + lo, hi = fp16(x), lo = fp16(x - hi): about 22 significant bits for
+// |x| in [2^-2, 2^15] (below, lo loses bits to fp16's subnormal range)
 #define SPLITH(x, HI, LO)                                   \
     do {                                                    \
         const float x_ = (x);                               \
@@ -136,14 +109,24 @@ template <> __device__ __forceinline__ void st_scalar<bf16_t>(bf16_t *p, size_t 
     } while (0)
 
 // ---------------------------------------------------------------- record
-// Per (chunk, head): for each wavefront role w (tokens 16w..16w+15 and
-// channels 32w..32w+31) 16 KB of fp16 fragments [operand][k-step][lane][8],
-// then d_t = q_t . k_t (fp32 [64]) and gamma (fp32 [128]). Records are
-// stored head-major (index head * records-per-head + chunk), so the records a
-// scan chain walks through are contiguous in memory.
+// Per (chunk, head): for each scan wavefront w (state channels 32w..32w+31,
+// tokens 16w..16w+15) 16 KB of fp16 MFMA fragments [operand][lane][8]:
+//   NW  (-W) for token tile tt = 0..3, k = w's channels    (W = IB Kd)
+//   QD  Qd for token tile tt = 0..3, k = w's channels
+//   KR  Kr^T for channel tile rt of w and token k-step ks   (index 2 rt + ks)
+//   IB  IB for w's tokens, token k-step ks (natural token order)
+//   MQ  strictly lower Mqk for w's tokens, token k-step ks
+// then d_t = q_t . k_t (fp32 [64]) and gamma (fp32 [128]). A "channel" k-step
+// gives lane (l16, lq) the channels 32w + 4lq + {0..3} and 32w + 16 + 4lq +
+// {0..3}, a "token" k-step ks of KR and MQ the tokens 32ks + 4lq + {0..3} and
+// 32ks + 16 + 4lq + {0..3}: exactly what that lane holds of two 16-row tiles
+// of the state (or of U) in MFMA output layout, so the scan feeds its own
+// accumulators to the next product without moving them. Records are stored
+// head-major (index head * records-per-head + chunk), so the records a scan
+// chain walks through are contiguous in memory.
 struct Rec {
     static constexpr int WAVE = 16384;
-    static constexpr int KD = 0, QD = 4096, IB = 8192, MQ = 10240, KR = 12288;
+    static constexpr int NW = 0, QD = 4096, KR = 8192, IB = 12288, MQ = 14336;
     static constexpr int DG = 4 * WAVE, GAM = DG + C * 4, BYTES = GAM + D * 4;
 };
 
@@ -223,10 +206,18 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
     float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
     _Float16 *sKrt = reinterpret_cast<_Float16 *>(smem + Lo::KRT);
+    // Kd^T [128][SKR] fp16, channel-major, built over the F tile once F is dead
+    _Float16 *sKdT = reinterpret_cast<_Float16 *>(smem + Lo::F);
+    static_assert(D * SKR * 2 <= C * SE * 4, "Kd^T fits over the F tile");
 
     const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // 8 wavefronts
     const int H = p.H;
-    const int items = p.sv.total_chunks() * H;
+    const int nchunks = p.sv.total_chunks();
+    const int items = nchunks * H;
+    // Items run from the last chunk to the first: the scan then starts on the
+    // records written last, which are still in the device's last-level cache
+    // (256 MB) when the whole set is larger.
+    auto chunk_of = [&](int item) { return nchunks - 1 - item / H; };
 
     // Inputs of one (chunk, head) item, fetched one item ahead. The loads are
     // issued unmasked (rows past the end read the last row) and masked when
@@ -244,7 +235,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     };
     int2 meta_ahead = {0, 0};
     if constexpr (VARLEN)
-        if ((int)blockIdx.x < items) meta_ahead = p.meta[(int)blockIdx.x / H];
+        if ((int)blockIdx.x < items) meta_ahead = p.meta[chunk_of(blockIdx.x)];
     u32x4 rq[2], rk[2];
     float rg[16];                // g of (token 16 (tid >> 7) + tt, channel tid & 127), tt < 16
     TB rbeta = TB(0);
@@ -254,11 +245,11 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     // stalls on a full vector-memory queue.
     auto fetch = [&](int item, int part) {
         if (part <= 0) {
-            const int ci = item / H;
+            const int ci = chunk_of(item);
             int2 m;
             if constexpr (VARLEN) {
                 m = meta_ahead;
-                meta_ahead = p.meta[min(item + (int)gridDim.x, items - 1) / H];
+                meta_ahead = p.meta[chunk_of(min(item + (int)gridDim.x, items - 1))];
             } else {
                 m = dense_meta(ci);
             }
@@ -303,7 +294,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     // an item: the compiler's wait for the next item's inputs then counts the
     // record stores issued after them and does not wait for those stores.
     auto body = [&](int item) __attribute__((always_inline)) {
-        const int ci = item / H, h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
+        const int ci = chunk_of(item), h = nx_h, tok0 = nx_tok0, Lc = nx_Lc;
         // per-thread LDS addresses are recomputed every item instead of being
         // hoisted out of the loop and held in registers for its whole length
         int tid = tid0;
@@ -573,32 +564,11 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // every later row at once, so the updates of a step are independent and the
         // L column reads (wave-uniform addresses) do not wait on the arithmetic.
         // Entries above the diagonal stay 0 (they only ever see x[sc] = 0).
-        // Meanwhile waves 4-7, idle until the record, build their role's Kd and
-        // Qd fragments (which do not depend on the inverse) and keep them in
-        // registers until the record is stored. (Qd moved into the first
-        // inverse level measured slower: that level then set the pace.)
+        // Meanwhile waves 4-7 (token tile tt = wave - 4), idle until the record,
+        // build what does not depend on the inverse: Kd^T for the W product (into
+        // LDS, over the F tile, which is dead now), and their tile's Qd and Mqk
+        // fragments, held in registers until the record is stored.
         f16x8 fr[8];
-        // x_t e^{a_t} (Kd from k, Qd from q) for the role's 16 tokens as four fp16
-        // A fragments: the chunk-start decay is G (chunk start -> block start)
-        // times E (block start -> t); rs: 1 / ||x_t|| (normalised input) or null
-        auto build_decayed = [&](const __bf16 *sx, const float *rs, f16x8 *dst) {
-            const int role = wave & 3, t = 16 * role + l16;
-            const float nr = NORM ? rs[t] : 1.f;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int c0 = 32 * ks + 8 * lq;
-                const bf16x8 xv = lds8(sx + t * SQ + c0);
-                const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
-                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + role * D + c0);
-                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + role * D + c0 + 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float dec = e < 4 ? g0[e] * e0[e] : g1[e - 4] * e1[e - 4];
-                    dst[ks][e] = static_cast<_Float16>((NORM ? bf2f(xv[e]) * nr : bf2f(xv[e])) * dec);
-                }
-            }
-        };
         if (wave < 4 && lane < 16) {
             const int I = wave, col = lane;
             float x[16];
@@ -612,8 +582,74 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             for (int tr = 0; tr < 16; ++tr)
                 if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
         } else if (wave >= 4) {
-            build_decayed(sK, NORM ? sRK : nullptr, fr);
-            build_decayed(sQ, NORM ? sRQ : nullptr, fr + 4);
+            const int tt = wave & 3;
+            // Kd^T = (k e^{a})^T, channel-major: a lane takes a token pair (16 tt +
+            // 2 (lane & 7), +1) and eight-channel groups lane >> 3 and (lane >> 3) + 8,
+            // and writes each (channel, token pair) as one dword. The chunk-start
+            // decay of token t is G (chunk start -> block start) times E (block
+            // start -> t).
+            {
+                const int t0 = 16 * tt + 2 * (lane & 7);
+                float nk0 = 1.f, nk1 = 1.f;
+                if constexpr (NORM) { nk0 = sRK[t0]; nk1 = sRK[t0 + 1]; }
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int c0 = 8 * ((lane >> 3) + 8 * gg);
+                    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0 + 4);
+                    const bf16x8 ka = lds8(sK + t0 * SQ + c0), kb = lds8(sK + (t0 + 1) * SQ + c0);
+                    const f32x4 ea0 = *reinterpret_cast<const f32x4 *>(sE + t0 * SE + c0);
+                    const f32x4 ea1 = *reinterpret_cast<const f32x4 *>(sE + t0 * SE + c0 + 4);
+                    const f32x4 eb0 = *reinterpret_cast<const f32x4 *>(sE + (t0 + 1) * SE + c0);
+                    const f32x4 eb1 = *reinterpret_cast<const f32x4 *>(sE + (t0 + 1) * SE + c0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float gg_ = e < 4 ? g0[e] : g1[e - 4];
+                        const float xa = bf2f(ka[e]) * nk0 * (e < 4 ? ea0[e] : ea1[e - 4]) * gg_;
+                        const float xb = bf2f(kb[e]) * nk1 * (e < 4 ? eb0[e] : eb1[e - 4]) * gg_;
+                        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+                        const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
+                        *reinterpret_cast<f16x2 *>(sKdT + (c0 + e) * SKR + t0) = pr;
+                    }
+                }
+            }
+            // Qd = q e^{a} for token tile tt, one fragment per scan wavefront w, in
+            // that wavefront's state-channel order (channels 32w + 4lq + {0..3},
+            // 32w + 16 + 4lq + {0..3})
+            {
+                const int t = 16 * tt + l16;
+                const float nr = NORM ? sRQ[t] : 1.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int c0 = 32 * w + 16 * hh + 4 * lq;
+                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(sQ + t * SQ + c0);
+                        const f32x4 e4 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            fr[w][4 * hh + i] = static_cast<_Float16>(bf2f(xv[i]) * nr * (g4[i] * e4[i]));
+                    }
+            }
+            // strictly lower Mqk for token tile tt in the scan's token order of U
+            // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
+            // the diagonal block are never written and are selected as zeros (a
+            // select, so stale LDS contents cannot leak in)
+            {
+                const int t = 16 * tt + l16;
+                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
+                        const bool zero = 2 * ks + hh > tt;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
+                    }
+            }
         }
         __syncthreads();
         fetch(next, 2);
@@ -690,56 +726,102 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             __syncthreads();
         }
 
-        // ================= record: fp16 fragments of the scan's left operands
-        // Record role r = wave & 3 (tokens 16r..16r+15, channels 32r..32r+31).
-        // Waves 4-7 built Kd and Qd above; waves 0-3 build Kr^T, IB and Mqk here.
-        // Both store eight fragments from the same code after the branch: stores
+        // ================= record: fp16 fragments of the scan's operands
+        // Wavefront p: token tile tt = p & 3. Waves 0-3 (scan wavefront w = p)
+        // build Kr^T and IB here; waves 4-7 built Qd and Mqk above. Every wave
+        // builds the IB fragments of its token tile, which are also the right
+        // operand of W^T = Kd^T IB^T, and forms W for the channel tiles
+        // 4 (p >> 2) .. +3 (scan wavefronts 2 (p >> 2) and 2 (p >> 2) + 1).
+        // Both roles then store eight fragments from the same code: stores
         // inside role branches would leave the compiler a path without them, and
         // its wait for the next item's inputs would then also wait for the stores.
         {
-            const int role = wave & 3;
-            const int t = 16 * role + l16;
+            const int tt = wave & 3;
+            const int t = 16 * tt + l16;
+            // IB[t][s] = INV[t][s] beta_s for s = 32ks + 8lq + e; INV[t][s] is stored
+            // at (s, t), zero for s > t. The read is unconditional (in bounds), so no
+            // branch waits on each of them.
+            f16x8 ib[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 be0 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq);
+                const f32x4 be1 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sc = 32 * ks + 8 * lq + e;
+                    const float x = sLI[sc * SL + t] * (e < 4 ? be0[e] : be1[e - 4]);
+                    ib[ks][e] = static_cast<_Float16>(sc <= t ? x : 0.f);
+                }
+            }
             if (wave < 4) {
-                // Kr^T fragments (channel rows, tokens 32ks + 8lq .. +7), from the
-                // channel-major tile written during the L / Mqk phase
+                // Kr^T fragments: rows = channels 32w + 16rt + l16, k = tokens of U's
+                // order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3})
+                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        fr[rt * 2 + ks] = lds8h(sKrt + (32 * role + 16 * rt + l16) * SKR + 32 * ks + 8 * lq);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const f32x4 be0 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq);
-                    const f32x4 be1 = *reinterpret_cast<const f32x4 *>(sBeta + 32 * ks + 8 * lq + 4);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int sc = 32 * ks + 8 * lq + e;
-                        // INV[t][sc] is stored at (sc, t); zero for sc > t. The read is
-                        // unconditional (in bounds), so no branch waits on each of them.
-                        const float x = sLI[sc * SL + t] * (e < 4 ? be0[e] : be1[e - 4]);
-                        fr[4 + ks][e] = static_cast<_Float16>(sc <= t ? x : 0.f);
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const _Float16 *row = sKrt + (32 * wave + 16 * rt + l16) * SKR + 32 * ks + 4 * lq;
+                        const f16x4_ a = *reinterpret_cast<const f16x4_ *>(row);
+                        const f16x4_ b = *reinterpret_cast<const f16x4_ *>(row + 16);
+                        fr[2 * rt + ks] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
                     }
-                    // Mqk blocks above the diagonal block are never written: select zeros
-                    // there (a select, so stale LDS contents cannot leak in)
-                    const f16x8 mq = *reinterpret_cast<const f16x8 *>(sMqk + t * SMQ + 32 * ks + 8 * lq);
-                    fr[6 + ks] = 2 * ks + (lq >> 1) > role ? f16x8{} : mq;
-                }
+                fr[4] = ib[0];
+                fr[5] = ib[1];
             }
-            // fragment i: waves 4-7 Kd (i < 4) and Qd, contiguous from KD; waves 0-3
-            // Kr (i < 4), then IB and Mqk, contiguous from IB
-            static_assert(Rec::QD == Rec::KD + 4096 && Rec::MQ == Rec::IB + 2048, "record layout");
-            char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES;
-            char *rw = rec + (size_t)role * Rec::WAVE + lane * 16;
-            const int o_lo = wave >= 4 ? Rec::KD : Rec::KR, o_hi = wave >= 4 ? Rec::KD : Rec::IB - 4096;
+            // W^T tiles (channels 16 ct .. +15) x (tokens of tile tt): Kd^T rows times
+            // IB^T; IB is lower triangular, so token tiles 0 and 1 need only the first
+            // 32 tokens. Output layout: lane (token t, channels 16ct + 4lq + {0..3}),
+            // which is the scan's channel order: channel tiles 2w and 2w + 1 give
+            // elements 0-3 and 4-7 of scan wavefront w's fragment.
+            {
+                const int ct0 = 4 * (wave >> 2);
+                f32x4 acc[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<f16x8 *>(rw + (i < 4 ? o_lo : o_hi) + i * 1024) = fr[i];
+                for (int c = 0; c < 4; ++c) {
+                    acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc[c] = mfma_f16(lds8h(sKdT + (16 * (ct0 + c) + l16) * SKR + 8 * lq), ib[0], acc[c]);
+                }
+                if (tt >= 2) {                                              // uniform
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[c] = mfma_f16(lds8h(sKdT + (16 * (ct0 + c) + l16) * SKR + 32 + 8 * lq), ib[1], acc[c]);
+                }
+                // stored negated: the scan forms U = U~ + (-W) M
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) fr[6 + j][e] = static_cast<_Float16>(-acc[2 * j + (e >> 2)][e & 3]);
+            }
+            // fragment i of wave p goes to (scan wavefront, byte offset in its part):
+            //   waves 0-3: Kr 0-3 -> (p, KR + i KB); IB 4-5 -> (p, IB + (i - 4) KB)
+            //   waves 4-7: Qd 0-3 -> (i, QD + tt KB); Mqk 4-5 -> (tt, MQ + (i - 4) KB)
+            //   both: W 6-7 -> (2 (p >> 2) + i - 6, NW + tt KB)
+            static_assert(Rec::IB == Rec::KR + 4096, "record layout");
+            char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES + lane * 16;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                int w_s, off;
+                if (i >= 6) {
+                    w_s = 2 * (wave >> 2) + i - 6;
+                    off = Rec::NW + tt * 1024;
+                } else if (wave < 4) {
+                    w_s = wave;
+                    off = Rec::KR + i * 1024;
+                } else {
+                    w_s = i < 4 ? i : tt;
+                    off = i < 4 ? Rec::QD + tt * 1024 : Rec::MQ + (i - 4) * 1024;
+                }
+                *reinterpret_cast<f16x8 *>(rec + (size_t)w_s * Rec::WAVE + off) = fr[i];
+            }
             // d (64 floats) then gamma (128 floats): one float per thread, every
             // thread issues the store and the range check drops those past the end
             static_assert(Rec::GAM == Rec::DG + C * 4, "record layout");
             const float tv = tid < C ? sDg[tid] : sGam[min(tid - C, D - 1) & (D - 1)];
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tv),
-                                                  buf_rsrc(rec + Rec::DG, (C + D) * 4), tid * 4, 0, 0);
+                                                  buf_rsrc(p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES + Rec::DG,
+                                                           (C + D) * 4),
+                                                  tid * 4, 0, 0);
         }
         __syncthreads();      // LDS is restaged by the next item
     };
@@ -753,18 +835,44 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 }
 
 // ---------------------------------------------------------------- scan
-constexpr int SMS = D + 8;       // fp16 row stride of the state       [col][136]
-constexpr int SYU = C + 8;       // fp16 row stride of Y and U         [col][72]
-constexpr int SVT = C + 8;       // bf16 row stride of the V tile      [col][72]
+// One workgroup per (sequence, head, TV-column tile); the chunks of the
+// sequence in order. Two roles of four wavefronts (one of each per SIMD),
+// sharing two barriers per chunk:
+//   recurrence wavefront w keeps state rows (channels) 32w..32w+31 in fp32
+//   accumulators. After barrier A (the state is in LDS) it forms U for its 16
+//   tokens, U = U~ - W M over all 128 channels, and puts U in LDS; after
+//   barrier B it updates its rows, M <- Diag(gamma) M + Kr^T U, puts them in
+//   LDS for the next chunk, and forms that chunk's U~ = IB V for its tokens
+//   (off the dependency chain, kept in registers).
+//   output wavefront w (tokens 16w..16w+15) forms o = Qd M + Mqk U + d U from
+//   the same LDS copies (Qd M between A and B, the rest after B) and stages
+//   the next chunk's V in LDS.
+// The two dependent contraction stages (U, then the state) are the whole
+// serial chain of a chunk. The state and U are split into fp16 hi + lo when
+// they are put in LDS (two products each, ~22 significant bits); the record's
+// fragments follow their register order, so every LDS read is one 16-byte read.
+//
+// Scale: the recurrence is linear in (V, S0), so the workgroup runs on V and
+// S0 scaled by a power of two 2^e chosen from the running maximum R of |S0|
+// and |V| (over its columns, up to the next chunk), such that R 2^e lies in
+// [64, 128): the fp16 parts keep their relative precision however small the
+// inputs are and do not overflow however large (65504 = 2^16 leaves 2^9 of
+// headroom for the state's growth over R). A change of e rescales the state
+// exactly (powers of two), and o, S_out and snapshots are scaled back.
+constexpr int NREC = 256;                // recurrence wavefronts, one per SIMD ...
+constexpr int SCAN_THR = 2 * NREC;       // ... and as many output wavefronts
+constexpr int SMS = D + 8;               // fp16 row stride of the state       [col][136]
+constexpr int SUS = C + 8;               // fp16 row stride of U               [col][72]
+constexpr int SVT = C + 8;               // bf16 row stride of the V tile      [col][72]
 
 template <int TV>
 struct ScanLds {
-    static constexpr int M = 0;                      // fp16 [2][TV][SMS] state hi / lo, [col][channel]
-    static constexpr int Y = M + 2 * TV * SMS * 2;   // fp16 [2][TV][SYU] (V - Kd M) hi / lo, [col][token]
-    static constexpr int U = Y + 2 * TV * SYU * 2;   // fp16 [2][TV][SYU] U hi / lo, [col][token]
-    static constexpr int V = U + 2 * TV * SYU * 2;   // bf16 [2][TV][SVT] V of a chunk, [col][token], double-buffered
-    static constexpr int DG = V + 2 * TV * SVT * 2;  // fp32 [2][C + D] d then gamma of a chunk, double-buffered
-    static constexpr int SIZE = DG + 2 * (C + D) * 4;
+    static constexpr int M = 0;                          // fp16 [2][TV][SMS] state hi / lo, [col][channel, register order]
+    static constexpr int U = M + 2 * TV * SMS * 2;       // fp16 [2][TV][SUS] U hi / lo, [col][token, register order]
+    static constexpr int UF = U + 2 * TV * SUS * 2;      // fp32 [C][TV + 4] U, [token][col] (the output's d U term)
+    static constexpr int V = UF + C * (TV + 4) * 4;      // bf16 [2][TV][SVT] V of a chunk, [col][token]
+    static constexpr int VMAX = V + 2 * TV * SVT * 2;    // fp32 [2][4] max |v| per output wavefront, then [4] max |S0|
+    static constexpr int SIZE = VMAX + 12 * 4;
 };
 
 struct ScanParams {
@@ -779,38 +887,47 @@ struct ScanParams {
     SnapView snap;
 };
 
-template <typename T> __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x);
-template <> __device__ __forceinline__ void buf_st4<float>(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, 0, 0);
-}
-template <> __device__ __forceinline__ void buf_st4<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[0])) |
-                        (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[1]))) << 16);
-    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2])) |
-                        (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[3]))) << 16);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, voff, 0, 0);
+// exponent e with R 2^e in [64, 128) (R > 0), clamped; 7 for R == 0
+__device__ __forceinline__ int scale_exp(float R) {
+    return min(100, max(-100, 7 - __builtin_amdgcn_frexp_expf(R)));
 }
 
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// max over the wavefront, on the vector ALU: rotations within rows of 16 lanes
+// (DPP row_ror 1, 2, 4, 8), then the four row maxima read as scalars
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f<0x121>(x));
+    x = fmaxf(x, dpp_f<0x122>(x));
+    x = fmaxf(x, dpp_f<0x124>(x));
+    x = fmaxf(x, dpp_f<0x128>(x));
+    const int b = __float_as_int(x);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
+__device__ __forceinline__ float max4(f32x4 x) { return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])); }
+
 template <int TV, typename TO>
-__global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WAVES) void chunk_scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = ScanLds<TV>;
     constexpr int NT = TV / 16;
     constexpr int TEAM = D / TV;
+    constexpr int VW = TV / 8;           // dwords of V per output thread and chunk (TV / 4 columns of one token)
     static_assert(TV == 16 || TV == 32, "value columns per workgroup");
-    constexpr int XP = NT;               // 16-byte pieces of V, d and gamma per lane and chunk
     _Float16 *sMh = reinterpret_cast<_Float16 *>(smem + Lo::M);
     _Float16 *sMl = sMh + TV * SMS;
-    _Float16 *sYh = reinterpret_cast<_Float16 *>(smem + Lo::Y);
-    _Float16 *sYl = sYh + TV * SYU;
     _Float16 *sUh = reinterpret_cast<_Float16 *>(smem + Lo::U);
-    _Float16 *sUl = sUh + TV * SYU;
+    _Float16 *sUl = sUh + TV * SUS;
+    float *sUf = reinterpret_cast<float *>(smem + Lo::UF);
     bf16_t *sV = reinterpret_cast<bf16_t *>(smem + Lo::V);
-    float *sDG = reinterpret_cast<float *>(smem + Lo::DG);
+    float *sVmax = reinterpret_cast<float *>(smem + Lo::VMAX);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
+    const int w4 = wave & 3;             // token tile (both roles) and state rows (recurrence)
     // XCD-aware placement: block b runs on XCD b % 8; the TEAM workgroups of
     // one chain share b % 8 and so one L2, where the chain's records are read.
     const int b = blockIdx.x;
@@ -822,333 +939,375 @@ __global__ __launch_bounds__(SCAN_THR, KDA_SCAN_MIN_WAVES) void chunk_scan_kerne
     const int col0 = member * TV;
     const int start = p.sv.seq_start(n), end = p.sv.seq_end(n);
     const int nch = (end - start + C - 1) / C, c0 = p.sv.first_chunk(n);
+    const int last = nch - 1;
     const size_t st_off = ((size_t)n * H + h) * D * D;
-    const int tb = 16 * (wave & 3);
     // bytes from a chunk's first row to the end of its last valid row
     auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
-
-    if (wave >= 4) {
-        // Output wavefronts: o = Qd M + Mqk U + d U for token tile tb, from the
-        // state and U that the recurrence wavefronts put in LDS, so that the
-        // recurrence's own steps carry only what the next chunk depends on. Their
-        // operands (Qd, Mqk) are loaded two chunks ahead, like the recurrence's;
-        // they pass the same barriers (one before the first chunk, three per
-        // chunk).
-        struct OFrags {
-            f16x8 qd[4], mq[2];
-            // 16-byte pieces of the chunk's V tile and of its d and gamma (adjacent
-            // in the record, 192 floats), staged through LDS one chunk ahead for
-            // the whole workgroup (stid: thread index in this group). TV = 16: one
-            // piece, wavefronts 4-5 V (token stid >> 1, columns 8 (stid & 1) ..
-            // +7), 6-7 d and gamma (floats 4 (stid - 128) .. +3; lanes past them
-            // repeat the last piece). TV = 32: piece 0 V (token stid >> 2, columns
-            // 8 (stid & 3) .. +7), piece 1 d and gamma (floats 4 stid .. +3,
-            // repeated past them).
-            u32x4 x[XP];
-        };
-        const int stid = tid - NTHR;
-        const bool x_is_v = TV == 32 || wave < 6;                  // uniform (piece 0)
-        static_assert(Rec::GAM == Rec::DG + C * 4, "d and gamma adjacent in the record");
-        constexpr int VL = TV / 8;                                 // lanes per V row
-        int x_off[XP];
-        x_off[0] = x_is_v ? ((stid / VL) * H * D + col0 + 8 * (stid % VL)) * 2
-                          : Rec::DG + 16 * min(stid - 128, (C + D) / 4 - 1);
-        if constexpr (XP == 2) x_off[XP - 1] = Rec::DG + 16 * min(stid, (C + D) / 4 - 1);
-        // the V / gamma piece of chunk j into LDS buffer j & 1 (read during step j)
-        auto stage = [&](const OFrags &f, int j) {
-            const int bsel = j & 1;
-            if (x_is_v) {
-                // transposed into [col][token]: one column of eight per 16-bit store
-                bf16_t *dst = sV + bsel * TV * SVT + (8 * (stid % VL)) * SVT + (stid / VL);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    dst[e * SVT] = static_cast<bf16_t>(e & 1 ? f.x[0][e >> 1] >> 16 : f.x[0][e >> 1] & 0xffffu);
-            }
-            const int dl = XP == 2 ? stid : stid - 128;            // lane's d / gamma piece
-            if ((XP == 2 || !x_is_v) && dl < (C + D) / 4)
-                *reinterpret_cast<u32x4 *>(sDG + bsel * (C + D) + 4 * dl) = f.x[XP - 1];
-        };
-        const int r_frag = (wave & 3) * Rec::WAVE + lane * 16;
-        // this lane's output: token tb + l16, columns col0 + 4lq .. +3 (O is formed transposed)
-        const int o_off = ((tb + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
-        auto oissue = [&](int j, OFrags &f) {
-            const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
-            const int tok0 = start + j * C, Lc = min(C, end - tok0);
-            // V rows past the end of the sequence read 0 (outside the range): their
-            // values never matter, because beta = 0 there makes the matching columns
-            // of IB zero
-            const auto rv = buf_rsrc(p.v + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, 2));
-#pragma unroll
-            for (int pc = 0; pc < XP; ++pc) f.x[pc] = buf_ld16<u32x4>(pc == 0 && x_is_v ? rv : rr, x_off[pc], 0);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) f.qd[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::QD + ks * 1024);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) f.mq[ks] = buf_ld16<f16x8>(rr, r_frag, Rec::MQ + ks * 1024);
-        };
-        auto ostep = [&](const OFrags &f, int j, const OFrags &f1, OFrags &nf, int nj) {
-            oissue(nj, nf);
-            stage(f1, j + 1);    // read by the recurrence in the next step
-            const int tok0 = start + j * C, Lc = min(C, end - tok0);
-            const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, sizeof(TO)));
-            const int bsel = j & 1;
-            __syncthreads();     // Y = V - Kd M is in LDS
-            // O^T = M^T Qd^T from the state at the chunk start (published before the
-            // barrier that ended the previous step, replaced only after the next
-            // one), while the recurrence forms U
-            f32x4 accO[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
-                    accO[nt] = mfma_f16(bh, f.qd[ks], accO[nt]);
-                    if constexpr (KDA_SPLIT_OI || TV == 16) {
-                        const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
-                        accO[nt] = mfma_f16(bl, f.qd[ks], accO[nt]);
-                    }
-                }
-            }
-            __syncthreads();     // U is in LDS
-            const float dt = sDG[bsel * (C + D) + tb + l16];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    // O^T += U^T Mqk^T (Mqk strictly lower)
-                    const f16x8 bh = lds8h(sUh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-                    accO[nt] = mfma_f16(bh, f.mq[ks], accO[nt]);
-                    if constexpr (KDA_SPLIT_UO || TV == 16) {
-                        const f16x8 bl = lds8h(sUl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-                        accO[nt] = mfma_f16(bl, f.mq[ks], accO[nt]);
-                    }
-                }
-                // + d_t U_t in fp32 for token tb + l16, columns 4lq .. +3, with U as its
-                // hi + lo parts (U to 2^-22 relative); one vector store (rows past
-                // the end are dropped)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int at = (16 * nt + 4 * lq + i) * SYU + tb + l16;
-                    accO[nt][i] += dt * (static_cast<float>(sUh[at]) + static_cast<float>(sUl[at]));
-                }
-                buf_st4<TO>(ro, o_off + 16 * nt * (int)sizeof(TO), accO[nt]);
-            }
-            __syncthreads();     // the next state is in LDS
-        };
-        if (nch > 0) {
-            const int last = nch - 1;
-            OFrags A, B, Cb;
-            oissue(0, A);
-            oissue(min(1, last), B);
-            stage(A, 0);
-            __syncthreads();     // the initial state and chunk 0's V / gamma are in LDS
-            for (int j = 0; j < nch; j += 3) {
-                ostep(A, j, B, Cb, min(j + 2, last));
-                if (j + 1 >= nch) break;
-                ostep(B, j + 1, Cb, A, min(j + 3, last));
-                if (j + 2 >= nch) break;
-                ostep(Cb, j + 2, A, B, min(j + 4, last));
-            }
-        }
-        return;
-    }
-
-    // state tile: wave w owns channels 32w..32w+31 (two 16-row tiles)
-    f32x4 Macc[2][NT];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int chn = 32 * wave + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                Macc[rt][nt][i] = p.S0 ? p.S0[st_off + (size_t)chn * D + col] : 0.f;
-            }
-    auto publish_state = [&]() {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                f16x4 hi, lo;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) SPLITH(Macc[rt][nt][i], hi[i], lo[i]);
-                const int col = 16 * nt + l16, chn = 32 * wave + 16 * rt + 4 * lq;
-                *reinterpret_cast<f16x4 *>(sMh + col * SMS + chn) = hi;
-                *reinterpret_cast<f16x4 *>(sMl + col * SMS + chn) = lo;
-            }
+    auto rec_rsrc = [&](int j) {
+        return buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
     };
-    publish_state();
+    const int r_lane = lane * 16;
+    // B-operand fragments from LDS: the state's k-step kk (channels of
+    // recurrence wavefront kk), U's token k-step ks
+    auto m_frag = [&](const _Float16 *base, int nt, int kk) { return lds8h(base + (16 * nt + l16) * SMS + 32 * kk + 8 * lq); };
+    auto u_frag = [&](const _Float16 *base, int nt, int ks) { return lds8h(base + (16 * nt + l16) * SUS + 32 * ks + 8 * lq); };
+    // U's position for token 16tt + 4lq + i: 32 (tt >> 1) + 8lq + 4 (tt & 1) + i
+    const int u_at = (l16 * SUS) + 32 * (w4 >> 1) + 8 * lq + 4 * (w4 & 1);
 
-    // operands of one chunk, loaded two chunks ahead
-    struct Frags {
-        f16x8 kd[4], ib[2], kr[2][2];
-    };
-    // loop-invariant byte offsets of this lane's record fragments
-    const int r_frag = wave * Rec::WAVE + lane * 16;
-
-    // The loads of one chunk's operands, as NLD slots in the order they are
-    // consumed: Kd by k-step, IB, Kr. issue() sends slots [s0, s1); the step
-    // spreads them over its phases, so that no wave stalls on a full
-    // vector-memory queue with work of its own waiting.
-    constexpr int NLD = 10;
-    auto issue = [&](int j, Frags &f, int s0, int s1) {
-        const auto rr = buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
-#pragma unroll
-        for (int sl = 0; sl < NLD; ++sl) {
-            if (sl < s0 || sl >= s1) continue;
-            if (sl < 4) {
-                f.kd[sl] = buf_ld16<f16x8>(rr, r_frag, Rec::KD + sl * 1024);
-            } else if (sl < 6) {
-                f.ib[sl - 4] = buf_ld16<f16x8>(rr, r_frag, Rec::IB + (sl - 4) * 1024);
-            } else {
-                const int e = sl - 6;
-                f.kr[e >> 1][e & 1] = buf_ld16<f16x8>(rr, r_frag, Rec::KR + e * 1024);
-            }
-            // keep the slot order: the in-order vmcnt then lets each use wait
-            // for its own load only
-            __builtin_amdgcn_sched_barrier(0x048F);
-        }
-    };
-    // where a step issues the next operands: Kd before its first product (START),
-    // IB after the first k-step of U (U0), Kr after the first k-step of the state
-    // update (M0)
-    enum { START, U0, M0 };
-    auto issue_at = [&](int nj, Frags &nf, int point) {
-        const int a = point == START ? 0 : point == U0 ? 4 : 6;
-        const int b = point == START ? 4 : point == U0 ? 6 : NLD;
-        issue(nj, nf, a, b);
-        // the loads stay where they are issued; compute and LDS traffic may cross
-        __builtin_amdgcn_sched_barrier(0x048F);
-    };
-    // Three operand buffers, used round-robin without copies: the loads for a chunk
-    // are issued two chunks before it is consumed (its V tile, d and gamma are put
-    // in LDS by the output wavefronts during the step before).
-    auto step = [&](const Frags &f, int j, const Frags &f1, Frags &nf, int nj) {
-        issue_at(nj, nf, START);
-        const int bsel = j & 1;
-
-        // X = Kd M for tokens tb..tb+15 (state split hi + lo)
-        f32x4 accX[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const f16x8 bh = lds8h(sMh + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
-                accX[nt] = mfma_f16(f.kd[ks], bh, accX[nt]);
-#if KDA_SPLIT_X
-                const f16x8 bl = lds8h(sMl + (16 * nt + l16) * SMS + 32 * ks + 8 * lq);
-                accX[nt] = mfma_f16(f.kd[ks], bl, accX[nt]);
-#endif
-            }
-            // V of tokens tb + 4lq .. +3 at this lane's column
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 vv = *reinterpret_cast<const u32x2 *>(sV + bsel * TV * SVT + (16 * nt + l16) * SVT + tb + 4 * lq);
-            f16x4 hi, lo;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t w = vv[i >> 1];
-                const float v = __uint_as_float(i & 1 ? w & 0xffff0000u : w << 16);
-                SPLITH(v - accX[nt][i], hi[i], lo[i]);
-            }
-            const int col = 16 * nt + l16, t = tb + 4 * lq;
-            *reinterpret_cast<f16x4 *>(sYh + col * SYU + t) = hi;
-            *reinterpret_cast<f16x4 *>(sYl + col * SYU + t) = lo;
-        }
-        __syncthreads();
-        // U = IB Y (Y split hi + lo)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f16x8 bh = lds8h(sYh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-                const f16x8 bl = lds8h(sYl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-                u = mfma_f16(f.ib[ks], bh, u);
-#if KDA_SPLIT_Y
-                u = mfma_f16(f.ib[ks], bl, u);
-#endif
-                if (nt == 0 && ks == 0) issue_at(nj, nf, U0);
-            }
-            f16x4 hi, lo;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) SPLITH(u[i], hi[i], lo[i]);
-            const int col = 16 * nt + l16, t = tb + 4 * lq;
-            *reinterpret_cast<f16x4 *>(sUh + col * SYU + t) = hi;
-            *reinterpret_cast<f16x4 *>(sUl + col * SYU + t) = lo;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            // M = Diag(gamma) M + Kr^T U for channels 32w..32w+31
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f32x4 gm = *reinterpret_cast<const f32x4 *>(sDG + bsel * (C + D) + C + 32 * wave + 16 * rt + 4 * lq);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Macc[rt][nt][i] *= gm[i];
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f16x8 bh = lds8h(sUh + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-                const f16x8 bl = lds8h(sUl + (16 * nt + l16) * SYU + 32 * ks + 8 * lq);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bh, Macc[rt][nt]);
-#if KDA_SPLIT_U
-                    Macc[rt][nt] = mfma_f16(f.kr[rt][ks], bl, Macc[rt][nt]);
-#endif
-                }
-                if (nt == 0 && ks == 0) issue_at(nj, nf, M0);
-            }
-        }
-        if (float *sp = p.snap.slot(n, h, H, j + 1, end - start, C, D * D)) {   // uniform across the workgroup
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int chn = 32 * wave + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                        sp[(size_t)chn * D + col] = Macc[rt][nt][i];
-                    }
-        }
-        publish_state();
-        __syncthreads();
-    };
-    // The prefetches are unconditional (the chunk index is clamped, so the tail
-    // re-reads the last record): conditional loads would make every later wait
-    // on vector memory conservative and defeat the prefetch.
-#if KDA_SCAN_BUFS == 3
-    Frags A, B, Cb;
-    if (nch > 0) {
-        const int last = nch - 1;
-        issue(0, A, 0, NLD);
-        issue(min(1, last), B, 0, NLD);
-        __syncthreads();
-        for (int j = 0; j < nch; j += 3) {
-            step(A, j, B, Cb, min(j + 2, last));
-            if (j + 1 >= nch) break;
-            step(B, j + 1, Cb, A, min(j + 3, last));
-            if (j + 2 >= nch) break;
-            step(Cb, j + 2, A, B, min(j + 4, last));
-        }
-    }
-#else
-    // two operand buffers: a chunk's loads are issued during the step before it
-#error "the V / gamma staging needs the next chunk's operands during a step: KDA_SCAN_BUFS must be 3"
-#endif
-
-    if (p.S_out) {
+    if (wave < 4) {
+        // ============================ recurrence
+        f32x4 Macc[2][NT];
+        float m0 = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int chn = 32 * wave + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                    p.S_out[st_off + (size_t)chn * D + col] = Macc[rt][nt][i];
+                    const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                    Macc[rt][nt][i] = p.S0 ? p.S0[st_off + (size_t)chn * D + col] : 0.f;
+                    m0 = fmaxf(m0, fabsf(Macc[rt][nt][i]));
                 }
+        if (nch == 0) {
+            // nothing to scan: S_out = S0 exactly
+            if (p.S_out)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                            p.S_out[st_off + (size_t)chn * D + col] = Macc[rt][nt][i];
+                        }
+            return;
+        }
+        m0 = wave_max(m0);
+        if (lane == 0) sVmax[8 + w4] = m0;
+        // the state into LDS (hi / lo, register order: channel 32w + 16rt + 4lq + i
+        // at position 32w + 8lq + 4rt + i)
+        auto publish = [&]() {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    f16x4 hi, lo;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) SPLITH(Macc[rt][nt][i], hi[i], lo[i]);
+                    const int at = (16 * nt + l16) * SMS + 32 * w4 + 8 * lq + 4 * rt;
+                    *reinterpret_cast<f16x4 *>(sMh + at) = hi;
+                    *reinterpret_cast<f16x4 *>(sMl + at) = lo;
+                }
+        };
+        struct Frags {
+            f16x8 nw[4], ib[2], kr[2][2];
+            f32x4 gm[2];
+        };
+        // The operand loads of one chunk as 12 slots: -W for this wavefront's
+        // token tile (k-step kk in recurrence wavefront kk's part of the
+        // record), IB, Kr^T and gamma (its own part). A step issues the next
+        // chunk's slots one at a time between its products: a burst of loads
+        // right after a barrier, from every wavefront at once, fills the CU's
+        // vector-memory queue and stalls the wavefronts in order.
+        auto issue = [&](__amdgpu_buffer_rsrc_t rr, Frags &f, int sl) __attribute__((always_inline)) {
+            if (sl < 4) f.nw[sl] = buf_ld16<f16x8>(rr, r_lane, sl * Rec::WAVE + Rec::NW + w4 * 1024);
+            else if (sl < 6) f.ib[sl - 4] = buf_ld16<f16x8>(rr, r_lane, w4 * Rec::WAVE + Rec::IB + (sl - 4) * 1024);
+            else if (sl < 10) f.kr[(sl - 6) >> 1][(sl - 6) & 1] = buf_ld16<f16x8>(rr, r_lane, w4 * Rec::WAVE + Rec::KR + (sl - 6) * 1024);
+            else f.gm[sl - 10] = buf_ld16<f32x4>(rr, Rec::GAM + (32 * w4 + 4 * lq) * 4, (sl - 10) * 64);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto issue_all = [&](int j, Frags &f) {
+            const auto rr = rec_rsrc(j);
+#pragma unroll
+            for (int sl = 0; sl < 12; ++sl) issue(rr, f, sl);
+        };
+        // U~ = IB (2^ex V) for this wavefront's tokens, from V in LDS buffer bsel
+        f32x4 ut[NT];
+        auto pseudo_values = [&](const Frags &f, int bsel, float sc) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                ut[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 vv = lds8(reinterpret_cast<const __bf16 *>(sV) + bsel * TV * SVT + (16 * nt + l16) * SVT +
+                                           32 * ks + 8 * lq);
+                    f16x8 vb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vb[e] = static_cast<_Float16>(bf2f(vv[e]) * sc);
+                    ut[nt] = mfma_f16(f.ib[ks], vb, ut[nt]);
+                }
+            }
+        };
+        float R = 0.f;
+        int ex = 0;
+        auto step = [&](Frags &f, int j, Frags &f1, Frags &nf, int nj) {
+            const auto rn = rec_rsrc(nj);
+            const int bsel = j & 1;
+            // U = U~ + (-W) M for tokens 16w4 .. +15
+            // (the hi and lo products accumulate in two chains of four)
+            f32x4 u[NT], ul_[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                u[nt] = ut[nt];
+                ul_[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    u[nt] = mfma_f16(f.nw[kk], m_frag(sMh, nt, kk), u[nt]);
+                    ul_[nt] = mfma_f16(f.nw[kk], m_frag(sMl, nt, kk), ul_[nt]);
+                }
+                issue(rn, nf, kk);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) u[nt] += ul_[nt];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f16x4 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    SPLITH(u[nt][i], hi[i], lo[i]);
+                    sUf[(16 * w4 + 4 * lq + i) * (TV + 4) + 16 * nt + l16] = u[nt][i];
+                }
+                *reinterpret_cast<f16x4 *>(sUh + u_at + 16 * nt * SUS) = hi;
+                *reinterpret_cast<f16x4 *>(sUl + u_at + 16 * nt * SUS) = lo;
+            }
+            issue(rn, nf, 4);
+            issue(rn, nf, 5);
+            __syncthreads();                                 // B: U (and the next chunk's V) are in LDS
+            R = fmaxf(R, max4(*reinterpret_cast<const f32x4 *>(sVmax + (bsel ^ 1) * 4)));
+            const int ex1 = scale_exp(R);
+            const float fs = __builtin_amdgcn_ldexpf(1.f, ex1 - ex);
+            // M <- Diag(gamma) M + Kr^T U for channels 32w4 .. +31, then into the
+            // next chunk's scale
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) Macc[rt][nt] *= f.gm[rt];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        Macc[rt][nt] = mfma_f16(f.kr[rt][ks], u_frag(sUh, nt, ks), Macc[rt][nt]);
+                        Macc[rt][nt] = mfma_f16(f.kr[rt][ks], u_frag(sUl, nt, ks), Macc[rt][nt]);
+                    }
+                    issue(rn, nf, 6 + 2 * rt + ks);
+                }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) Macc[rt][nt] *= fs;
+            ex = ex1;
+            if (float *sp = p.snap.slot(n, h, H, j + 1, end - start, C, D * D)) {   // uniform across the workgroup
+                const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                            sp[(size_t)chn * D + col] = Macc[rt][nt][i] * inv;
+                        }
+            }
+            publish();
+            issue(rn, nf, 10);
+            issue(rn, nf, 11);
+            // the next chunk's U~ (its V is in LDS since barrier B), in its scale
+            pseudo_values(f1, bsel ^ 1, __builtin_amdgcn_ldexpf(1.f, ex));
+            __syncthreads();                                 // A: the next state is in LDS
+        };
+        Frags A, B, Cb;
+        issue_all(0, A);
+        issue_all(min(1, last), B);
+        __syncthreads();                                     // S0 and chunk 0's V (and their maxima) are in LDS
+        R = fmaxf(max4(*reinterpret_cast<const f32x4 *>(sVmax + 8)), max4(*reinterpret_cast<const f32x4 *>(sVmax)));
+        ex = scale_exp(R);
+        {
+            const float s0 = __builtin_amdgcn_ldexpf(1.f, ex);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) Macc[rt][nt] *= s0;
+            publish();
+            pseudo_values(A, 0, s0);
+        }
+        __syncthreads();                                     // A: the initial state is in LDS
+        // Rounds of six steps (two turns of the three operand buffers): at the
+        // loop's back edge the compiler waits for more of the prefetched
+        // operands than a step needs, so the back edge is kept rare.
+        for (int j = 0; j < nch; j += 6) {
+            step(A, j, B, Cb, min(j + 2, last));
+            if (j + 1 >= nch) break;
+            step(B, j + 1, Cb, A, min(j + 3, last));
+            if (j + 2 >= nch) break;
+            step(Cb, j + 2, A, B, min(j + 4, last));
+            if (j + 3 >= nch) break;
+            step(A, j + 3, B, Cb, min(j + 5, last));
+            if (j + 4 >= nch) break;
+            step(B, j + 4, Cb, A, min(j + 6, last));
+            if (j + 5 >= nch) break;
+            step(Cb, j + 5, A, B, min(j + 7, last));
+        }
+        if (p.S_out) {
+            const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
+                        p.S_out[st_off + (size_t)chn * D + col] = Macc[rt][nt][i] * inv;
+                    }
+        }
+        return;
     }
+
+    // ============================ output
+    if (nch == 0) return;
+    const int stid = tid - NREC;         // 0 .. 255
+    // the operands of chunk c; vr holds the V of chunk c as well, loaded three
+    // chunks ahead (it comes from HBM, the records mostly from cache)
+    struct OFrags {
+        f16x8 qd[4], mq[2];
+        float dv;                        // d of token 16w4 + l16
+        uint32_t vr[VW];                 // V of token stid >> 2, columns col0 + (TV / 4)(stid & 3) ..
+    };
+    const int v_off = ((stid >> 2) * H * D + col0 + (TV / 4) * (stid & 3)) * 2;
+    auto vissue = [&](int j, OFrags &f) {
+        const int tok0 = start + j * C, Lc = min(C, end - tok0);
+        // V rows past the end of the sequence read 0 (outside the range)
+        const auto rv = buf_rsrc(p.v + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, 2));
+        if constexpr (VW == 2) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0));
+            f.vr[0] = x[0]; f.vr[1] = x[1];
+        } else {
+            const u32x4 x = buf_ld16<u32x4>(rv, v_off, 0);
+#pragma unroll
+            for (int i = 0; i < VW; ++i) f.vr[i] = x[i];
+        }
+        __builtin_amdgcn_sched_barrier(0x048F);
+    };
+    // the record loads as 7 slots: Qd (k-step kk in recurrence wavefront kk's
+    // part), Mqk, d; issued one at a time between the products, like the
+    // recurrence's
+    auto oissue = [&](__amdgpu_buffer_rsrc_t rr, OFrags &f, int sl) __attribute__((always_inline)) {
+        if (sl < 4) f.qd[sl] = buf_ld16<f16x8>(rr, r_lane, sl * Rec::WAVE + Rec::QD + w4 * 1024);
+        else if (sl < 6) f.mq[sl - 4] = buf_ld16<f16x8>(rr, r_lane, w4 * Rec::WAVE + Rec::MQ + (sl - 4) * 1024);
+        else f.dv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, Rec::DG + (16 * w4 + l16) * 4, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto oissue_all = [&](int j, OFrags &f) {
+        const auto rr = rec_rsrc(j);
+#pragma unroll
+        for (int sl = 0; sl < 7; ++sl) oissue(rr, f, sl);
+    };
+    // V of a chunk into LDS buffer bsel, transposed to [col][token], and this
+    // wavefront's max |v| of it into slot bsel
+    auto stage_v = [&](const OFrags &f, int bsel) {
+        bf16_t *dst = sV + bsel * TV * SVT + ((TV / 4) * (stid & 3)) * SVT + (stid >> 2);
+        float vm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 2 * VW; ++e) {
+            const uint32_t wv = f.vr[e >> 1];
+            const bf16_t x = static_cast<bf16_t>(e & 1 ? wv >> 16 : wv & 0xffffu);
+            dst[e * SVT] = x;
+            vm = fmaxf(vm, fabsf(bf16_to_f32(x)));
+        }
+        vm = wave_max(vm);
+        if (lane == 0) sVmax[bsel * 4 + w4] = vm;
+    };
+    // this lane's outputs: token 16w4 + l16, columns col0 + 16nt + 4lq .. +3
+    const int o_base = ((16 * w4 + l16) * H * D + col0 + 4 * lq) * (int)sizeof(TO);
+    float R = 0.f;
+    int ex = 0;
+    // L2 warming: the TEAM workgroups of a chain read every record, on one XCD.
+    // Three chunks ahead, each output wavefront touches one dword of every
+    // 128-byte line of its share of the record, so that the records' lines are
+    // in L2 when the operand loads arrive. The touched values are folded into a
+    // register one step later (that load is then long complete) and kept alive
+    // to the end by an empty asm that takes them as input.
+    constexpr int LPW = Rec::DG / 128 / (4 * TEAM);                 // lines per wavefront
+    const int touch_off = ((member * 4 + w4) * LPW + lane % LPW) * 128;  // < Rec::DG
+    uint32_t touch_acc = 0, touch_prev = 0;
+    auto ostep = [&](OFrags &f, int j, const OFrags &f1, OFrags &nf, int nj) {
+        const int bsel = j & 1;
+        touch_acc ^= touch_prev;
+        touch_prev = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(j + 3, last)), touch_off, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_v(f1, bsel ^ 1);           // the next chunk's V and its max
+        vissue(min(j + 3, last), f);     // this buffer's chunk after next: j + 3
+        // o^T (part) = M^T Qd^T from the state at the chunk start (in LDS since
+        // barrier A), formed transposed so that a lane holds four consecutive
+        // columns of one token; the hi and lo products in two chains
+        // (o only: the state's fp16 hi part, 11 significant bits, is enough here)
+        const auto rn = rec_rsrc(nj);
+        f32x4 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f16(m_frag(sMh, nt, kk), f.qd[kk], acc[nt]);
+            oissue(rn, nf, kk);
+        }
+        __syncthreads();                                     // B: U (and the next chunk's V) are in LDS
+        R = fmaxf(R, max4(*reinterpret_cast<const f32x4 *>(sVmax + (bsel ^ 1) * 4)));
+        // o = Qd M + Mqk U + d U in this chunk's scale; back to input units
+        const int tok0 = start + j * C, Lc = min(C, end - tok0);
+        const auto ro = buf_rsrc(static_cast<TO *>(p.out) + ((size_t)tok0 * H + h) * D, chunk_bytes(Lc, sizeof(TO)));
+        const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
+        const float d_t = f.dv;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            // o^T += U^T Mqk^T (U's hi part), then d_t U[t] in fp32: token
+            // t = 16w4 + l16, columns 16nt + 4lq + i
+            f32x4 o = acc[nt];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                o = mfma_f16(u_frag(sUh, nt, ks), f.mq[ks], o);
+                if (nt == NT - 1) oissue(rn, nf, 4 + ks);
+            }
+            const f32x4 uf = *reinterpret_cast<const f32x4 *>(sUf + (16 * w4 + l16) * (TV + 4) + 16 * nt + 4 * lq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (o[i] + d_t * uf[i]) * inv;
+            buf_st4<TO>(ro, o_base + 16 * nt * (int)sizeof(TO), o);
+        }
+        oissue(rn, nf, 6);
+        ex = scale_exp(R);
+        __syncthreads();                                     // A: the next state is in LDS
+    };
+    OFrags A, B, Cb;
+    vissue(0, A);
+    oissue_all(0, A);
+    vissue(min(1, last), B);
+    oissue_all(min(1, last), B);
+    vissue(min(2, last), Cb);
+    stage_v(A, 0);
+    __syncthreads();                                         // S0 and chunk 0's V (and their maxima) are in LDS
+    R = fmaxf(max4(*reinterpret_cast<const f32x4 *>(sVmax + 8)), max4(*reinterpret_cast<const f32x4 *>(sVmax)));
+    ex = scale_exp(R);
+    __syncthreads();                                         // A: the initial state is in LDS
+    // rounds of six steps, as for the recurrence
+    for (int j = 0; j < nch; j += 6) {
+        ostep(A, j, B, Cb, min(j + 2, last));
+        if (j + 1 >= nch) break;
+        ostep(B, j + 1, Cb, A, min(j + 3, last));
+        if (j + 2 >= nch) break;
+        ostep(Cb, j + 2, A, B, min(j + 4, last));
+        if (j + 3 >= nch) break;
+        ostep(A, j + 3, B, Cb, min(j + 5, last));
+        if (j + 4 >= nch) break;
+        ostep(B, j + 4, Cb, A, min(j + 6, last));
+        if (j + 5 >= nch) break;
+        ostep(Cb, j + 5, A, B, min(j + 7, last));
+    }
+    asm volatile("" ::"v"(touch_acc ^ touch_prev));
 }
 
 // ---------------------------------------------------------------- host
@@ -1221,11 +1380,16 @@ hipError_t run(const PrefillArgs &a) {
         const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
         ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc,
                       SnapView{a.snaps, a.snap_every, a.max_snaps}};
-        if (wide)
-            hipLaunchKernelGGL((chunk_scan_kernel<32, TO>), dim3(blocks), dim3(SCAN_THR), ScanLds<32>::SIZE, a.stream, sp);
-        else
-            hipLaunchKernelGGL((chunk_scan_kernel<16, TO>), dim3(blocks), dim3(SCAN_THR), ScanLds<16>::SIZE, a.stream, sp);
-        return hipGetLastError();
+        auto launch = [&](auto kern, int lds) {
+            // set on every call (idempotent; no process-wide "already set" flag to race on)
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(blocks), dim3(SCAN_THR), lds, a.stream, sp);
+            return hipGetLastError();
+        };
+        return wide ? launch(chunk_scan_kernel<32, TO>, ScanLds<32>::SIZE)
+                    : launch(chunk_scan_kernel<16, TO>, ScanLds<16>::SIZE);
     }
 }
 

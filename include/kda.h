@@ -131,10 +131,19 @@ size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int
  *     kernels address one chunk of a token-major tensor with 32-bit offsets);
  *   io_dtype KDA_F32: fp32 arithmetic throughout, beta_dtype and out_dtype
  *     must be KDA_F32;
- *   io_dtype KDA_BF16: bf16 q/k/v with bf16 MFMA contractions and fp32
- *     accumulation/state, beta_dtype KDA_BF16 or KDA_F32, out_dtype KDA_BF16
- *     or KDA_F32 (a bf16 `out` is the round-to-nearest-even of the fp32
- *     value the same kernel would store).
+ *   io_dtype KDA_BF16: bf16 q/k/v, beta_dtype KDA_BF16 or KDA_F32, out_dtype
+ *     KDA_BF16 or KDA_F32 (a bf16 `out` is the round-to-nearest-even of the
+ *     fp32 value the same kernel would store). At Dk = Dv = 128, C = 64 the
+ *     contractions run on fp16 MFMA (the state and U split into fp16 hi + lo
+ *     parts, about 22 significant bits, where they feed the state) and fp32
+ *     MFMA, with fp32 accumulation and an fp32 state; other bf16 shapes run
+ *     fp32 arithmetic.
+ *   Value range of the bf16 path: v and S0 of any magnitude (each (sequence,
+ *     head, value-column tile) is scaled internally by a power of two from the
+ *     running maximum of |S0| and |v|; tested from 1e-7 to 1e3). q and k rows
+ *     of L2 norm at most 16 (their products are held in fp16; L2-normalised
+ *     inputs, or the qk_l2norm option, satisfy this). As for the recurrence
+ *     itself, a step is a contraction only while beta_t ||k_t||^2 <= 2.
  *
  * workspace: device buffer of at least kda_prefill_workspace_size(...) bytes
  * (may be NULL when that size is 0), 256-byte aligned. Its contents on entry

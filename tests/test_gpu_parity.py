@@ -296,3 +296,18 @@ def test_prefill_exact_decay_path_plain_kernel():
     blk = torch.stack([torch.exp(p.g[0, a:a + 16, 2]).prod(0).min() for a in range(0, 192, 16)])
     assert bool((blk < 1.17549435e-38).any()) and bool((blk >= 1.17549435e-38).any())
     run_and_check(p, TOL_BF16, label="exact decay path (plain kda_prefill)")
+
+
+@pytest.mark.parametrize("scale", [1e3, 1e-3, 1e-5, 1e-7])
+@pytest.mark.parametrize("gate", ["softplus", "slow"])
+def test_prefill_value_range(scale, gate):
+    """v and S0 far from unit magnitude. The MFMA path holds the state, V - W M and U in
+    fp16 parts, which on their own lose precision below ~2^-14 and overflow above 65504;
+    the kernels scale each column tile by a power of two from the running maximum of
+    |S0| and |v|, so the tolerance holds at every scale. Packed ragged sequences, both
+    scan tile widths' shapes (12 packed sequences x 16 heads takes the 32-column tiles)."""
+    from dataclasses import replace
+    for lengths, H in (([300, 77, 130], 4), ([130, 0, 64, 1, 257, 191, 65, 128, 320, 63, 200, 96], 16)):
+        p = inputs.prefill(H, 128, lengths=lengths, C=64, io="bf16", s0_std=0.3, seed=61, gate=gate)
+        p = replace(p, v=(p.v.float() * scale).to(torch.bfloat16), S0=p.S0 * scale)
+        run_and_check(p, TOL_BF16, label=f"value scale {scale:g}, gate {gate}, {len(lengths)} sequences")
