@@ -2,10 +2,15 @@
 
 A step is one kda_prefill of the single-sequence workload (B=1, H=32,
 T=8192, D=128, C=64, bf16 q/k/v/o and beta, fp32 g and state), inputs
-already resident in HBM. The JSON line also carries the decode workload
-(512 sequences x 32 heads, D=128, 64 in-place steps) measured the same way,
-the roofline of the dominant kernel, and the fp64 CPU oracle timed on the
-host cores as a reference baseline.
+already resident in HBM. The JSON line also carries:
+  * the other two prefill workloads (16 packed sequences with initial states;
+    one 1,048,576-token sequence at H=16), each with its own roofline;
+  * a cold-cache figure for the single-sequence workload (the device's 256 MB
+    last-level cache flushed by a 512 MB write before every timed call);
+  * the decode workload (512 sequences x 32 heads, D=128, 64 in-place steps);
+  * the output norm and gate over the prefill output;
+  * the roofline of the dominant unit, and the fp64 CPU oracle timed on the
+    host cores as a reference baseline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -27,8 +32,10 @@ from gated_delta_rule_103_amd.kda import kda_prefill_workspace_size  # noqa: E40
 
 PREFILL_WORKLOAD = "single_seq_8k"
 DECODE_WORKLOAD = "decode_512x32"
-# arithmetic type of the timed prefill path: bf16 MFMA contractions, fp32 accumulation and state
-PREFILL_DTYPE = "bf16"
+# arithmetic of the timed prefill path (bf16 is only the I/O type)
+PREFILL_DTYPE = ("fp16 MFMA (state and U split into fp16 hi+lo) + fp32 MFMA, fp32 accumulate and state; "
+                 "bf16 q/k/v/o")
+EXTRA_PREFILL_WORKLOADS = ("varlen_16x", "long_1m")
 
 
 # Every leg's untimed warmup lasts at least this long (and at least `warmup`
@@ -87,6 +94,53 @@ def bench_prefill(steps, warmup, workload=PREFILL_WORKLOAD):
     min_bytes = costs.prefill_min_bytes(tokens, H, D, D, N, io_bytes=2, beta_bytes=2, has_s0=p.S0 is not None)
     return dict(tokens=tokens, seqs=N, wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=ms,
                 flops=flops, min_bytes=min_bytes, inputs=p)
+
+
+def bench_prefill_cold(reps, workload=PREFILL_WORKLOAD):
+    """One kda_prefill per rep with the device's last-level cache (256 MB) flushed first
+    by writing a 512 MB buffer; each call timed alone with an event pair on the launch
+    stream, the flush outside it. Returns the median ms per call."""
+    p = inputs.workload_prefill(workload, device="cuda")
+    w = inputs.WORKLOADS[workload]
+    B, T, H, D, C = p.q.shape[0], p.q.shape[1], w["H"], w["D"], w["C"]
+    N = p.num_seqs
+    out = torch.empty(B, T, H, D, dtype=torch.bfloat16, device="cuda")
+    S_out = torch.empty(N, H, D, D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(kda_prefill_workspace_size(N, B * T, H, D, D, C, torch.bfloat16), 1), dtype=torch.uint8,
+                     device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for r in range(reps + 2):
+        flush.fill_(r & 0xff)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        kda_prefill(p.q, p.k, p.v, p.g, p.beta, p.S0, out=out, S_out=S_out, cu_seqlens=p.cu_seqlens, C=C,
+                    workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            times.append(a.elapsed_time(b))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def prefill_leg(pf, workload):
+    """Rate and rooflines of one timed prefill workload (a bench_prefill result)."""
+    w = inputs.WORKLOADS[workload]
+    k_s = pf["kernel_ms"] * 1e-3
+    tflops = pf["flops"] / k_s / 1e12
+    gbps = pf["min_bytes"] / k_s / 1e9
+    peak_tf, peak_bw = costs.MI355X_PEAK["bf16_TFLOPs"], costs.MI355X_PEAK["hbm_GBps"]
+    return {"sequences": pf["seqs"], "tokens": pf["tokens"], "H": w["H"],
+            "ms_per_call": round(pf["kernel_ms"], 4),
+            "mtok_per_s": round(pf["tokens"] / k_s / 1e6, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                         "frac": round(tflops / peak_tf, 4),
+                         "traffic": measured_traffic("kda_prefill", workload),
+                         "model": "12C^3+8C^2D+6CD^2 FLOP per chunk-head"},
+            "roofline_hbm": {"bound": "hbm", "achieved": round(gbps, 1), "peak": peak_bw, "unit": "GB/s",
+                             "frac": round(gbps / peak_bw, 4), "bytes": pf["min_bytes"],
+                             "model": "algorithmic minimum bytes per launch"}}
 
 
 def bench_decode(steps, warmup):
@@ -179,6 +233,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--workload", default=PREFILL_WORKLOAD, choices=["single_seq_8k", "varlen_16x", "long_1m"],
                     help="prefill workload to time (the metric is quoted on single_seq_8k)")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the other two prefill workloads and the cold-cache leg")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the bench, run a plain device copy of MIB MiB three times "
                          "(the known-size reference that scales HBM counter readings)")
@@ -198,6 +254,18 @@ def main():
     tflops = pf["flops"] / k_s / 1e12
     gbps = pf["min_bytes"] / k_s / 1e9
     value = pf["tokens"] * args.steps / pf["wall_s"] / 1e6
+    extra = {}
+    cold_ms = None
+    if not args.no_extra_workloads and args.workload == PREFILL_WORKLOAD:
+        for wl in EXTRA_PREFILL_WORKLOADS:
+            # the 1M-token workload's call takes ~30 ms: fewer calls
+            st = max(2, args.steps // 4) if wl == "long_1m" else args.steps
+            r = bench_prefill(st, min(args.warmup, 2), wl)
+            del r["inputs"]
+            torch.cuda.empty_cache()
+            extra[wl] = prefill_leg(r, wl)
+            extra[wl]["steps"] = st
+        cold_ms = bench_prefill_cold(max(5, args.steps // 2))
     dec = None if args.no_decode else bench_decode(max(1, args.steps // 4), 1)
     og = bench_output_gate(args.steps, args.warmup, (pf["tokens"], w_h := inputs.WORKLOADS[args.workload]["H"],
                                                      inputs.WORKLOADS[args.workload]["D"]))
@@ -232,6 +300,13 @@ def main():
                          "frac": round(gbps / peak_bw, 4),
                          "bytes": pf["min_bytes"], "model": "algorithmic minimum bytes per launch"},
     }
+    if cold_ms is not None:
+        line["cold_cache"] = {"workload": args.workload, "ms_per_call": round(cold_ms, 4),
+                              "mtok_per_s": round(pf["tokens"] / (cold_ms * 1e-3) / 1e6, 3),
+                              "note": "last-level cache (256 MB) flushed by a 512 MB write before each call; "
+                                      "median of single calls"}
+    if extra:
+        line["prefill_workloads"] = extra
     if dec is not None:
         line["decode"] = {"workload": DECODE_WORKLOAD, "ms_per_token_step": round(dec["ms_per_token_step"], 4),
                           "roofline": {"bound": "hbm", "achieved": round(dec["gbps_state"], 1),
