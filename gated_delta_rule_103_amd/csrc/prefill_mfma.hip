@@ -21,13 +21,17 @@
 //       blocks and fp32 MFMA products off it; W = IB Kd on fp16 MFMA; and a
 //       record of the scan's operands in fp16, laid out as MFMA fragments in
 //       the register order of the scan's accumulators.
-// scan  (one workgroup of four wavefronts per (sequence, head, 16- or
-//       32-column value tile), its chunks in order): each wavefront keeps 32
-//       rows of the fp32 state in registers; per chunk it forms its share of
-//       U (and of Qd M) over those rows, the four shares meet in LDS at the
-//       step's one barrier, and every wavefront then updates its rows and forms
-//       o for its 16 tokens. Contractions on fp16 MFMA with the state and U
-//       split into fp16 hi + lo, fp32 accumulation.
+// scan  (one workgroup of eight wavefronts per (sequence, head, 16- or
+//       32-column value tile), its chunks in order): four recurrence
+//       wavefronts keep 32 rows of the fp32 state each in registers and form
+//       U = U~ - W M, the state update and the next chunk's U~; four output
+//       wavefronts form o = Qd M + Mqk U + d U for 16 tokens each. The state
+//       and U meet in LDS at two barriers per chunk. Contractions on fp16 MFMA
+//       with the state and U split into fp16 hi + lo, fp32 accumulation; V and
+//       S0 scaled by a power of two from their running maximum.
+// One long sequence runs as a pipeline over windows of chunks: the prep of the
+// next window (second stream, the CUs the scan leaves free) beside the scan of
+// the current one, with the records of two windows in the workspace.
 //
 // Every decay factor that is formed is <= 1, except on the diagonal 16x16
 // blocks of L and Mqk, which use the block's own start as reference: their
@@ -169,6 +173,7 @@ struct PrepParams {
     char *rec;
     long long rec_stride;        // records per head (head-major record layout)
     float norm_eps;              // NORM: q_t / sqrt(||q_t||^2 + eps), the same for k_t
+    int cw0, cwn;                // window: global chunks cw0 .. cw0 + cwn - 1; record index chunk - cw0
 };
 
 // {first token, length} of every chunk of packed sequences (zeros past the last)
@@ -212,14 +217,17 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 
     const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // 8 wavefronts
     const int H = p.H;
-    const int nchunks = p.sv.total_chunks();
-    const int items = nchunks * H;
+    // the chunks of this launch's window that exist
+    const int wn = max(0, min(p.sv.total_chunks(), p.cw0 + p.cwn) - p.cw0);
+    const int items = wn * H;
     // Items run from the last chunk to the first: the scan then starts on the
     // records written last, which are still in the device's last-level cache
     // (256 MB) when the whole set is larger.
-    auto chunk_of = [&](int item) { return nchunks - 1 - item / H; };
+    auto chunk_of = [&](int item) { return p.cw0 + wn - 1 - item / H; };
 
-    // Inputs of one (chunk, head) item, fetched one item ahead. The loads are
+    // Inputs of one (chunk, head) item, fetched one item ahead, and the record
+    // stores, carry the non-temporal hint (each byte is touched once here; the
+    // hint keeps them from displacing lines the scan still reads). The loads are
     // issued unmasked (rows past the end read the last row) and masked when
     // staged, and the next fetch is unconditional (clamped item index): a load
     // that is used right away or issued under a branch makes the compiler wait
@@ -263,8 +271,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             for (int it = 0; it < 2; ++it) {
                 const int idx = tid0 + it * PTHR, row = idx >> 4, part = idx & 15;
                 const size_t off = ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 8 * part;
-                rq[it] = *reinterpret_cast<const u32x4 *>(p.q + off);
-                rk[it] = *reinterpret_cast<const u32x4 *>(p.k + off);
+                rq[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.q + off));
+                rk[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k + off));
             }
         }
         if (part == -1 || part == 1) {
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 const auto rgc = buf_rsrc(p.g + ((size_t)tok0 * H + h) * D, ((Lc - 1) * H + 1) * D * 4);
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt)
-                    rg[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgc, (min(16 * I + tt, Lc - 1) * H * D + c) * 4, 0, 0));
+                    rg[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgc, (min(16 * I + tt, Lc - 1) * H * D + c) * 4, 0, 2));
             }
         }
         if (part == -1 || part == 2)
@@ -798,7 +806,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             //   waves 4-7: Qd 0-3 -> (i, QD + tt KB); Mqk 4-5 -> (tt, MQ + (i - 4) KB)
             //   both: W 6-7 -> (2 (p >> 2) + i - 6, NW + tt KB)
             static_assert(Rec::IB == Rec::KR + 4096, "record layout");
-            char *rec = p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES + lane * 16;
+            char *rec = p.rec + ((size_t)h * p.rec_stride + ci - p.cw0) * Rec::BYTES + lane * 16;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 int w_s, off;
@@ -812,16 +820,16 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     w_s = i < 4 ? i : tt;
                     off = i < 4 ? Rec::QD + tt * 1024 : Rec::MQ + (i - 4) * 1024;
                 }
-                *reinterpret_cast<f16x8 *>(rec + (size_t)w_s * Rec::WAVE + off) = fr[i];
+                __builtin_nontemporal_store(fr[i], reinterpret_cast<f16x8 *>(rec + (size_t)w_s * Rec::WAVE + off));
             }
             // d (64 floats) then gamma (128 floats): one float per thread, every
             // thread issues the store and the range check drops those past the end
             static_assert(Rec::GAM == Rec::DG + C * 4, "record layout");
             const float tv = tid < C ? sDg[tid] : sGam[min(tid - C, D - 1) & (D - 1)];
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tv),
-                                                  buf_rsrc(p.rec + ((size_t)h * p.rec_stride + ci) * Rec::BYTES + Rec::DG,
+                                                  buf_rsrc(p.rec + ((size_t)h * p.rec_stride + ci - p.cw0) * Rec::BYTES + Rec::DG,
                                                            (C + D) * 4),
-                                                  tid * 4, 0, 0);
+                                                  tid * 4, 0, 2);
         }
         __syncthreads();      // LDS is restaged by the next item
     };
@@ -885,6 +893,11 @@ struct ScanParams {
     const char *rec;
     long long rec_stride;        // records per head
     SnapView snap;
+    // window: global chunks cw0 .. cw0 + cwn - 1 (record index chunk - cw0). A
+    // chain whose chunks continue past the window leaves its state in S_run, and
+    // one whose chunks began before it takes its state from there.
+    float *S_run;
+    int cw0, cwn;
 };
 
 // exponent e with R 2^e in [64, 128) (R > 0), clamped; 7 for R == 0
@@ -939,12 +952,17 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     const int col0 = member * TV;
     const int start = p.sv.seq_start(n), end = p.sv.seq_end(n);
     const int nch = (end - start + C - 1) / C, c0 = p.sv.first_chunk(n);
-    const int last = nch - 1;
+    // this launch's chunks j0 .. j1 - 1 of the sequence, and where its state
+    // comes from and goes to
+    const int j0 = min(nch, max(0, p.cw0 - c0)), j1 = min(nch, max(0, p.cw0 + p.cwn - c0));
+    const int last = j1 - 1;
+    const float *S_in = j0 == 0 ? p.S0 : p.S_run;
+    float *S_fin = j1 == nch ? p.S_out : p.S_run;
     const size_t st_off = ((size_t)n * H + h) * D * D;
     // bytes from a chunk's first row to the end of its last valid row
     auto chunk_bytes = [&](int Lc, int elem) { return ((Lc - 1) * H * D + D) * elem; };
     auto rec_rsrc = [&](int j) {
-        return buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j) * Rec::BYTES, Rec::BYTES);
+        return buf_rsrc(p.rec + ((size_t)h * p.rec_stride + c0 + j - p.cw0) * Rec::BYTES, Rec::BYTES);
     };
     const int r_lane = lane * 16;
     // B-operand fragments from LDS: the state's k-step kk (channels of
@@ -965,12 +983,12 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                    Macc[rt][nt][i] = p.S0 ? p.S0[st_off + (size_t)chn * D + col] : 0.f;
+                    Macc[rt][nt][i] = S_in ? S_in[st_off + (size_t)chn * D + col] : 0.f;
                     m0 = fmaxf(m0, fabsf(Macc[rt][nt][i]));
                 }
-        if (nch == 0) {
-            // nothing to scan: S_out = S0 exactly
-            if (p.S_out)
+        if (j0 >= j1) {
+            // nothing to scan in this launch; an empty sequence: S_out = S0 exactly
+            if (nch == 0 && p.S_out)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -1121,8 +1139,8 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
             __syncthreads();                                 // A: the next state is in LDS
         };
         Frags A, B, Cb;
-        issue_all(0, A);
-        issue_all(min(1, last), B);
+        issue_all(j0, A);
+        issue_all(min(j0 + 1, last), B);
         __syncthreads();                                     // S0 and chunk 0's V (and their maxima) are in LDS
         R = fmaxf(max4(*reinterpret_cast<const f32x4 *>(sVmax + 8)), max4(*reinterpret_cast<const f32x4 *>(sVmax)));
         ex = scale_exp(R);
@@ -1139,20 +1157,20 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
         // Rounds of six steps (two turns of the three operand buffers): at the
         // loop's back edge the compiler waits for more of the prefetched
         // operands than a step needs, so the back edge is kept rare.
-        for (int j = 0; j < nch; j += 6) {
+        for (int j = j0; j < j1; j += 6) {
             step(A, j, B, Cb, min(j + 2, last));
-            if (j + 1 >= nch) break;
+            if (j + 1 >= j1) break;
             step(B, j + 1, Cb, A, min(j + 3, last));
-            if (j + 2 >= nch) break;
+            if (j + 2 >= j1) break;
             step(Cb, j + 2, A, B, min(j + 4, last));
-            if (j + 3 >= nch) break;
+            if (j + 3 >= j1) break;
             step(A, j + 3, B, Cb, min(j + 5, last));
-            if (j + 4 >= nch) break;
+            if (j + 4 >= j1) break;
             step(B, j + 4, Cb, A, min(j + 6, last));
-            if (j + 5 >= nch) break;
+            if (j + 5 >= j1) break;
             step(Cb, j + 5, A, B, min(j + 7, last));
         }
-        if (p.S_out) {
+        if (S_fin) {
             const float inv = __builtin_amdgcn_ldexpf(1.f, -ex);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
@@ -1161,14 +1179,14 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                        p.S_out[st_off + (size_t)chn * D + col] = Macc[rt][nt][i] * inv;
+                        S_fin[st_off + (size_t)chn * D + col] = Macc[rt][nt][i] * inv;
                     }
         }
         return;
     }
 
     // ============================ output
-    if (nch == 0) return;
+    if (j0 >= j1) return;
     const int stid = tid - NREC;         // 0 .. 255
     // the operands of chunk c; vr holds the V of chunk c as well, loaded three
     // chunks ahead (it comes from HBM, the records mostly from cache)
@@ -1283,28 +1301,28 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
         __syncthreads();                                     // A: the next state is in LDS
     };
     OFrags A, B, Cb;
-    vissue(0, A);
-    oissue_all(0, A);
-    vissue(min(1, last), B);
-    oissue_all(min(1, last), B);
-    vissue(min(2, last), Cb);
+    vissue(j0, A);
+    oissue_all(j0, A);
+    vissue(min(j0 + 1, last), B);
+    oissue_all(min(j0 + 1, last), B);
+    vissue(min(j0 + 2, last), Cb);
     stage_v(A, 0);
     __syncthreads();                                         // S0 and chunk 0's V (and their maxima) are in LDS
     R = fmaxf(max4(*reinterpret_cast<const f32x4 *>(sVmax + 8)), max4(*reinterpret_cast<const f32x4 *>(sVmax)));
     ex = scale_exp(R);
     __syncthreads();                                         // A: the initial state is in LDS
     // rounds of six steps, as for the recurrence
-    for (int j = 0; j < nch; j += 6) {
+    for (int j = j0; j < j1; j += 6) {
         ostep(A, j, B, Cb, min(j + 2, last));
-        if (j + 1 >= nch) break;
+        if (j + 1 >= j1) break;
         ostep(B, j + 1, Cb, A, min(j + 3, last));
-        if (j + 2 >= nch) break;
+        if (j + 2 >= j1) break;
         ostep(Cb, j + 2, A, B, min(j + 4, last));
-        if (j + 3 >= nch) break;
+        if (j + 3 >= j1) break;
         ostep(A, j + 3, B, Cb, min(j + 5, last));
-        if (j + 4 >= nch) break;
+        if (j + 4 >= j1) break;
         ostep(B, j + 4, Cb, A, min(j + 6, last));
-        if (j + 5 >= nch) break;
+        if (j + 5 >= j1) break;
         ostep(Cb, j + 5, A, B, min(j + 7, last));
     }
     asm volatile("" ::"v"(touch_acc ^ touch_prev));
@@ -1327,6 +1345,38 @@ hipError_t device_cus(int *cus) {
 size_t ws_offs(int N) { return ((sizeof(int32_t) * (size_t)(N + 1) + 255) / 256) * 256; }
 size_t ws_meta(long long maxc) { return ((sizeof(int2) * (size_t)maxc + 255) / 256) * 256; }
 
+// One long sequence runs as a pipeline over windows of WIN chunks: the prep of
+// window w + 1 (on a second stream, on the CUs the scan leaves free) overlaps
+// the scan of window w, and the records of only two windows exist at a time.
+// The chain's state passes from window to window through S_run.
+constexpr long long WIN = 512;
+// (maxc - 1: the chunks of one sequence; max_chunks counts one more per sequence)
+bool windowed(int N, long long maxc) { return N == 1 && maxc - 1 >= 4 * WIN; }
+size_t ws_records(int N, long long maxc, int H) {
+    return (size_t)(windowed(N, maxc) ? 2 * WIN : maxc) * H * Rec::BYTES;
+}
+size_t ws_state(int N, long long maxc, int H) {
+    return windowed(N, maxc) ? (size_t)H * D * D * sizeof(float) : 0;
+}
+
+// The events and the stream of one pipelined call, released on every exit
+// path. Destruction does not wait: the runtime releases them once the work
+// queued on them has completed.
+struct Pipeline {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[5] = {};
+    ~Pipeline() {
+        for (hipEvent_t e : ev)
+            if (e) (void)hipEventDestroy(e);
+        if (side) (void)hipStreamDestroy(side);
+    }
+    hipError_t init() {
+        for (hipEvent_t &e : ev)
+            if (const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming); r != hipSuccess) return r;
+        return hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+    }
+};
+
 template <typename TB, typename TO>
 hipError_t run(const PrefillArgs &a) {
     const long long maxc = max_chunks(a.N, (long long)a.B * a.T, C);
@@ -1334,6 +1384,7 @@ hipError_t run(const PrefillArgs &a) {
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws);
     int2 *meta = reinterpret_cast<int2 *>(ws + ws_offs(a.N));
     char *recs = ws + ws_offs(a.N) + ws_meta(maxc);
+    float *S_run = reinterpret_cast<float *>(recs + ws_records(a.N, maxc, a.H));
     SeqView sv{a.cu_seqlens, chunk_off, a.N, a.T, C};
     const bool varlen = a.cu_seqlens != nullptr;
     int cus = 0;
@@ -1346,51 +1397,101 @@ hipError_t run(const PrefillArgs &a) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    {
-        // kernel variant [varlen][per-head gate][L2-normalised q, k]
-        using Kern = void (*)(PrepParams);
-        const Kern kerns[2][2][2] = {
-            {{chunk_prep_kernel<TB, false, false, false>, chunk_prep_kernel<TB, false, false, true>},
-             {chunk_prep_kernel<TB, false, true, false>, chunk_prep_kernel<TB, false, true, true>}},
-            {{chunk_prep_kernel<TB, true, false, false>, chunk_prep_kernel<TB, true, false, true>},
-             {chunk_prep_kernel<TB, true, true, false>, chunk_prep_kernel<TB, true, true, true>}}};
-        const Kern kern = kerns[varlen][a.g_head][a.qk_norm];
-        // set on every call (idempotent; no process-wide "already set" flag to race on)
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+    // kernel variant [varlen][per-head gate][L2-normalised q, k]
+    using PrepKern = void (*)(PrepParams);
+    const PrepKern kerns[2][2][2] = {
+        {{chunk_prep_kernel<TB, false, false, false>, chunk_prep_kernel<TB, false, false, true>},
+         {chunk_prep_kernel<TB, false, true, false>, chunk_prep_kernel<TB, false, true, true>}},
+        {{chunk_prep_kernel<TB, true, false, false>, chunk_prep_kernel<TB, true, false, true>},
+         {chunk_prep_kernel<TB, true, true, false>, chunk_prep_kernel<TB, true, true, true>}}};
+    const PrepKern prep_kern = kerns[varlen][a.g_head][a.qk_norm];
+    // 16 value columns per scan workgroup, or 32 when the 16-column workgroups
+    // would fill the CUs four times over or more (many chains, e.g. packed
+    // batches): a CU then reads each record once per 32 columns instead of per 16
+    const int chains = a.N * a.H;
+    const bool wide = (long long)chains * (D / 16) >= 4LL * cus;
+    const int team = wide ? D / 32 : D / 16;
+    const unsigned scan_blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
+    using ScanKern = void (*)(ScanParams);
+    const ScanKern scan_kern = wide ? chunk_scan_kernel<32, TO> : chunk_scan_kernel<16, TO>;
+    const int scan_lds = wide ? ScanLds<32>::SIZE : ScanLds<16>::SIZE;
+    // set on every call (idempotent; no process-wide "already set" flag to race on)
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prep_kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
-        if (e != hipSuccess) return e;
+        e != hipSuccess)
+        return e;
+    if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
+        e != hipSuccess)
+        return e;
+
+    // prep of global chunks cw0 .. cw0 + cwn - 1 into `slot` (cwn records per head)
+    auto prep = [&](long long cw0, long long cwn, char *slot, unsigned max_grid, hipStream_t st) {
         PrepParams pp{static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k), a.g, a.beta, sv, meta,
-                      a.H, recs, maxc, a.norm_eps};
-        // persistent: one workgroup per CU walks the (chunk, head) items
-        const long long items = maxc * a.H;
-        const unsigned grid = (unsigned)std::min<long long>(items, cus);
-        if (items > 0) {
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(PTHR), PrepLds::SIZE, a.stream, pp);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
+                      a.H, slot, cwn, a.norm_eps, (int)cw0, (int)cwn};
+        // persistent: at most one workgroup per CU walks the (chunk, head) items
+        const unsigned grid = (unsigned)std::min<long long>(cwn * a.H, max_grid);
+        hipLaunchKernelGGL(prep_kern, dim3(grid), dim3(PTHR), PrepLds::SIZE, st, pp);
+        return hipGetLastError();
+    };
+    auto scan = [&](long long cw0, long long cwn, const char *slot, hipStream_t st) {
+        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, slot, cwn,
+                      SnapView{a.snaps, a.snap_every, a.max_snaps}, S_run, (int)cw0, (int)cwn};
+        hipLaunchKernelGGL(scan_kern, dim3(scan_blocks), dim3(SCAN_THR), scan_lds, st, sp);
+        return hipGetLastError();
+    };
+
+    if (!windowed(a.N, maxc)) {
+        if (maxc * a.H > 0)
+            if (hipError_t e = prep(0, maxc, recs, (unsigned)cus, a.stream); e != hipSuccess) return e;
+        return scan(0, maxc, recs, a.stream);
+    }
+
+    // Windowed pipeline. Slot w % 2 holds window w's records; the prep of window
+    // w waits for the scan of window w - 2 (the slot's previous reader), the
+    // scan of window w for the prep of window w. While a stream capture is
+    // under way on the caller's stream everything stays on that stream (no
+    // overlap, same results).
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipError_t e = hipStreamIsCapturing(a.stream, &cap); e != hipSuccess) return e;
+    const bool concurrent = cap == hipStreamCaptureStatusNone;
+    Pipeline pl;     // created only outside a capture
+    if (concurrent)
+        if (hipError_t e = pl.init(); e != hipSuccess) return e;
+    hipStream_t ps = concurrent ? pl.side : a.stream;
+    hipEvent_t ev_in = pl.ev[0], ev_prep[2] = {pl.ev[1], pl.ev[2]}, ev_scan[2] = {pl.ev[3], pl.ev[4]};
+    // the prep stream starts after the caller's earlier work (inputs, chunk table)
+    if (concurrent) {
+        if (hipError_t e = hipEventRecord(ev_in, a.stream); e != hipSuccess) return e;
+        if (hipError_t e = hipStreamWaitEvent(ps, ev_in, 0); e != hipSuccess) return e;
+    }
+    // the scan's workgroups, spread one per CU, leave cus - scan_blocks CUs to the
+    // preps that overlap it (all CUs when the scan takes more than half)
+    const unsigned side_grid = scan_blocks * 2 <= (unsigned)cus ? (unsigned)cus - scan_blocks : (unsigned)cus;
+    const long long nwin = (maxc + WIN - 1) / WIN;
+    auto windows = [&]() -> hipError_t {
+        for (long long w = 0; w < nwin; ++w) {
+            char *slot = recs + (size_t)(w & 1) * WIN * a.H * Rec::BYTES;
+            const long long cw0 = w * WIN, cwn = std::min(WIN, maxc - cw0);
+            if (concurrent && w >= 2)
+                if (hipError_t e = hipStreamWaitEvent(ps, ev_scan[w & 1], 0); e != hipSuccess) return e;
+            if (hipError_t e = prep(cw0, cwn, slot, w == 0 ? (unsigned)cus : side_grid, ps); e != hipSuccess)
+                return e;
+            if (concurrent) {
+                if (hipError_t e = hipEventRecord(ev_prep[w & 1], ps); e != hipSuccess) return e;
+                if (hipError_t e = hipStreamWaitEvent(a.stream, ev_prep[w & 1], 0); e != hipSuccess) return e;
+            }
+            if (hipError_t e = scan(cw0, cwn, slot, a.stream); e != hipSuccess) return e;
+            if (concurrent)
+                if (hipError_t e = hipEventRecord(ev_scan[w & 1], a.stream); e != hipSuccess) return e;
         }
-    }
-    {
-        // 16 value columns per workgroup, or 32 when the 16-column workgroups would
-        // fill the CUs four times over or more (many chains, e.g. packed batches):
-        // a CU then reads each record once per 32 columns instead of per 16
-        const int chains = a.N * a.H;
-        const bool wide = (long long)chains * (D / 16) >= 4LL * cus;
-        const int team = wide ? D / 32 : D / 16;
-        const unsigned blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
-        ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, recs, maxc,
-                      SnapView{a.snaps, a.snap_every, a.max_snaps}};
-        auto launch = [&](auto kern, int lds) {
-            // set on every call (idempotent; no process-wide "already set" flag to race on)
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(blocks), dim3(SCAN_THR), lds, a.stream, sp);
-            return hipGetLastError();
-        };
-        return wide ? launch(chunk_scan_kernel<32, TO>, ScanLds<32>::SIZE)
-                    : launch(chunk_scan_kernel<16, TO>, ScanLds<16>::SIZE);
-    }
+        return hipSuccess;
+    };
+    const hipError_t err = windows();
+    // whatever happened, later work on the caller's stream follows everything
+    // queued on the side stream
+    if (concurrent && hipEventRecord(ev_in, ps) == hipSuccess) (void)hipStreamWaitEvent(a.stream, ev_in, 0);
+    return err;
 }
 
 template <typename TB>
@@ -1401,8 +1502,10 @@ hipError_t run_o(const PrefillArgs &a) {
 }  // namespace
 
 size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C_) {
-    if (Dk == D && Dv == D && C_ == C)
-        return ws_offs(N) + ws_meta(max_chunks(N, T_total, C)) + (size_t)max_chunks(N, T_total, C) * H * Rec::BYTES;
+    if (Dk == D && Dv == D && C_ == C) {
+        const long long maxc = max_chunks(N, T_total, C);
+        return ws_offs(N) + ws_meta(maxc) + ws_records(N, maxc, H) + ws_state(N, maxc, H);
+    }
     return prefill_f32_workspace(N, T_total, H, Dk, Dv, C_);
 }
 

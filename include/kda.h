@@ -97,7 +97,9 @@ const char *kda_status_string(int status);
  * Bytes of device workspace kda_prefill needs for these sizes. A pure host
  * function of its arguments (0 is a valid answer). T_total is the number of
  * tokens over all sequences (B*T for dense input). Returns 0 for sizes
- * kda_prefill would reject.
+ * kda_prefill would reject. On the MFMA shapes it is about 66 KB per
+ * (chunk, head), except for one long sequence (see kda_prefill), where it is
+ * that of two windows of 512 chunks plus one fp32 state per head.
  */
 size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int C,
                                   kda_dtype io_dtype);
@@ -149,6 +151,17 @@ size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int
  * (may be NULL when that size is 0), 256-byte aligned. Its contents on entry
  * are ignored; it must not be used by anything else until the call's work
  * on `stream` has finished.
+ *
+ * One long sequence (N == 1 with at least 2,048 chunks, on the fp16/fp32 MFMA
+ * shapes) runs as a pipeline over windows of 512 chunks: the per-chunk
+ * operands of only two windows exist at a time, so the workspace stops
+ * growing with T_total, and the preparation of the next window runs on a
+ * second HIP stream, beside the scan of the current one on the CUs the scan
+ * leaves free. That stream and five events are created by the call and
+ * released by the runtime once their work has completed; all of the call's
+ * work is ordered after earlier work on `stream`, and later work on `stream`
+ * after all of it. While `stream` is being captured into a HIP graph the
+ * pipeline runs on `stream` alone (same results, no overlap).
  */
 int kda_prefill(const void *q, const void *k, const void *v, const float *g,
                 const void *beta, const float *S0, void *out, float *S_out,

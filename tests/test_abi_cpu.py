@@ -97,6 +97,23 @@ def test_prefill_workspace_misaligned(lib):
     assert lib.kda_prefill_workspace_size(1, 8192, 32, 128, 128, 64, 1) >= 129 * 32 * 65536
 
 
+def test_workspace_of_one_long_sequence_is_bounded(lib):
+    """One sequence of at least 2,048 chunks runs in windows of 512 chunks: its workspace
+    holds two windows of 66,304-byte records and one fp32 state per head, whatever its
+    length; two sequences of the same length keep one record per (chunk, head)."""
+    T = 4 * 512 * 64 + 6 * 64 + 37
+    one = lib.kda_prefill_workspace_size(1, T, 2, 128, 128, 64, 1)
+    longer = lib.kda_prefill_workspace_size(1, 8 * T, 2, 128, 128, 64, 1)
+    rec = 2 * 512 * 2 * 66304
+    assert rec + 2 * 128 * 128 * 4 <= one < rec + 2 * 128 * 128 * 4 + (1 << 20)
+    assert 0 <= longer - one < (1 << 20)
+    assert lib.kda_prefill_workspace_size(2, 2 * T, 2, 128, 128, 64, 1) >= 2 * 2055 * 2 * 66304
+    # just below the threshold (2,047 chunks) the records cover every chunk
+    assert lib.kda_prefill_workspace_size(1, 2047 * 64, 2, 128, 128, 64, 1) >= 2047 * 2 * 66304
+    # the long-context workload: 1,048,576 tokens at H = 16, about 1.09 GB instead of 17.4 GB
+    assert lib.kda_prefill_workspace_size(1, 1 << 20, 16, 128, 128, 64, 1) < 1_100_000_000
+
+
 def test_workspace_size_is_pure_and_rejects_bad_sizes(lib):
     a = lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 0)
     assert a > 0 and a == lib.kda_prefill_workspace_size(16, 135000, 32, 128, 128, 64, 0)
