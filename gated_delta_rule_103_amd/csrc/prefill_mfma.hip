@@ -1258,7 +1258,6 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
         touch_acc ^= touch_prev;
         touch_prev = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(j + 3, last)), touch_off, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        stage_v(f1, bsel ^ 1);           // the next chunk's V and its max
         vissue(min(j + 3, last), f);     // this buffer's chunk after next: j + 3
         // o^T (part) = M^T Qd^T from the state at the chunk start (in LDS since
         // barrier A), formed transposed so that a lane holds four consecutive
@@ -1297,6 +1296,10 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
             buf_st4<TO>(ro, o_base + 16 * nt * (int)sizeof(TO), o);
         }
         oissue(rn, nf, 6);
+        // V of chunk j + 2 and its max into the buffer chunk j's V has left (read
+        // before barrier A of this step); staged here, after barrier B, where
+        // this wavefront waits for the recurrence anyway
+        stage_v(nf, bsel);
         ex = scale_exp(R);
         __syncthreads();                                     // A: the next state is in LDS
     };
@@ -1307,6 +1310,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     oissue_all(min(j0 + 1, last), B);
     vissue(min(j0 + 2, last), Cb);
     stage_v(A, 0);
+    stage_v(B, 1);
     __syncthreads();                                         // S0 and chunk 0's V (and their maxima) are in LDS
     R = fmaxf(max4(*reinterpret_cast<const f32x4 *>(sVmax + 8)), max4(*reinterpret_cast<const f32x4 *>(sVmax)));
     ex = scale_exp(R);
@@ -1350,6 +1354,9 @@ size_t ws_meta(long long maxc) { return ((sizeof(int2) * (size_t)maxc + 255) / 2
 // the scan of window w, and the records of only two windows exist at a time.
 // The chain's state passes from window to window through S_run.
 constexpr long long WIN = 512;
+// window starts stay even: the scan's V double buffer is indexed by chunk parity
+// from a prologue that stages the first chunk's V into buffer 0
+static_assert(WIN % 2 == 0, "even window length");
 // (maxc - 1: the chunks of one sequence; max_chunks counts one more per sequence)
 bool windowed(int N, long long maxc) { return N == 1 && maxc - 1 >= 4 * WIN; }
 size_t ws_records(int N, long long maxc, int H) {
