@@ -1456,12 +1456,15 @@ hipError_t run(const PrefillArgs &a) {
 
     // Windowed pipeline. Slot w % 2 holds window w's records; the prep of window
     // w waits for the scan of window w - 2 (the slot's previous reader), the
-    // scan of window w for the prep of window w. While a stream capture is
-    // under way on the caller's stream everything stays on that stream (no
-    // overlap, same results).
+    // scan of window w for the prep of window w. The preps overlap the scans
+    // only where the scan's workgroups, one per CU, leave half of the CUs free
+    // (a prep that took CUs the scan needs would hold back part of its chains
+    // for a whole window); otherwise, and while a stream capture is under way
+    // on the caller's stream, everything runs in order on that stream (same
+    // results, bounded workspace).
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipError_t e = hipStreamIsCapturing(a.stream, &cap); e != hipSuccess) return e;
-    const bool concurrent = cap == hipStreamCaptureStatusNone;
+    const bool concurrent = cap == hipStreamCaptureStatusNone && scan_blocks * 2 <= (unsigned)cus;
     Pipeline pl;     // created only outside a capture
     if (concurrent)
         if (hipError_t e = pl.init(); e != hipSuccess) return e;
@@ -1473,8 +1476,8 @@ hipError_t run(const PrefillArgs &a) {
         if (hipError_t e = hipStreamWaitEvent(ps, ev_in, 0); e != hipSuccess) return e;
     }
     // the scan's workgroups, spread one per CU, leave cus - scan_blocks CUs to the
-    // preps that overlap it (all CUs when the scan takes more than half)
-    const unsigned side_grid = scan_blocks * 2 <= (unsigned)cus ? (unsigned)cus - scan_blocks : (unsigned)cus;
+    // preps that overlap it
+    const unsigned side_grid = concurrent ? (unsigned)cus - scan_blocks : (unsigned)cus;
     const long long nwin = (maxc + WIN - 1) / WIN;
     auto windows = [&]() -> hipError_t {
         for (long long w = 0; w < nwin; ++w) {

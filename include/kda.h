@@ -155,13 +155,14 @@ size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int
  * One long sequence (N == 1 with at least 2,048 chunks, on the fp16/fp32 MFMA
  * shapes) runs as a pipeline over windows of 512 chunks: the per-chunk
  * operands of only two windows exist at a time, so the workspace stops
- * growing with T_total, and the preparation of the next window runs on a
- * second HIP stream, beside the scan of the current one on the CUs the scan
- * leaves free. That stream and five events are created by the call and
- * released by the runtime once their work has completed; all of the call's
- * work is ordered after earlier work on `stream`, and later work on `stream`
- * after all of it. While `stream` is being captured into a HIP graph the
- * pipeline runs on `stream` alone (same results, no overlap).
+ * growing with T_total. Where the scan (64 workgroups per 8 heads) leaves at
+ * least half of the CUs free (H <= 16 on 256 CUs), the preparation of the next window
+ * runs on a second HIP stream beside the scan of the current one; that stream
+ * and five events are created by the call and released by the runtime once
+ * their work has completed, all of the call's work is ordered after earlier
+ * work on `stream`, and later work on `stream` after all of it. Otherwise, and
+ * while `stream` is being captured into a HIP graph, the windows run in order
+ * on `stream` alone (same results).
  */
 int kda_prefill(const void *q, const void *k, const void *v, const float *g,
                 const void *beta, const float *S0, void *out, float *S_out,

@@ -103,6 +103,19 @@ def test_windowed_per_head_gate():
     assert eo <= TOL_BF16["o"] and eS <= TOL_BF16["S"]
 
 
+def test_windowed_many_heads_in_order():
+    """32 heads: the scan takes every CU, so the windows run in order on the caller's
+    stream (no side stream); every token and head against the oracle."""
+    p = inputs.prefill(32, 128, B=1, T=T_LONG, C=C, io="bf16", s0_std=0.02, seed=307)
+    say(f"[windowed] in order: T={T_LONG} H=32")
+    d = to_dev(p)
+    o, S = kda_prefill(d.q, d.k, d.v, d.g, d.beta, d.S0, C=C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rS = oracle_prefill(p)
+    eo, eS = _errs(o, S, ro, rS)
+    assert eo <= TOL_BF16["o"] and eS <= TOL_BF16["S"]
+
+
 def test_windowed_snapshots_across_window_borders():
     """Snapshots every 300 chunks: slots 1..6 fall inside windows 0..3 at varying
     offsets; slots 7 and 8 lie past the end and stay untouched."""
