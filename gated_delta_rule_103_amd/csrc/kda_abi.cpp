@@ -107,6 +107,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     a.g_head = g_head;
     a.qk_norm = qk_norm;
     a.norm_eps = norm_eps;
+    a.in_order = noalloc;
     if (snapshots) {
         a.snaps = snapshots;
         a.snap_every = snapshot_every / C;

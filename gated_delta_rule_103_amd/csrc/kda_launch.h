@@ -34,6 +34,9 @@ struct PrefillArgs {
     // L2-normalise q and k over Dk inside the kernels: x / sqrt(sum x^2 + norm_eps)
     bool qk_norm = false;
     float norm_eps = 0.f;
+    // run everything on `stream` (no side stream or events created), as for
+    // callers that must not create runtime objects (the no-allocation entry)
+    bool in_order = false;
 };
 
 struct DecodeArgs {

@@ -1460,11 +1460,11 @@ hipError_t run(const PrefillArgs &a) {
     // only where the scan's workgroups, one per CU, leave half of the CUs free
     // (a prep that took CUs the scan needs would hold back part of its chains
     // for a whole window); otherwise, and while a stream capture is under way
-    // on the caller's stream, everything runs in order on that stream (same
-    // results, bounded workspace).
+    // on the caller's stream or for a caller that asked for it (in_order),
+    // everything runs in order on that stream (same results, bounded workspace).
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipError_t e = hipStreamIsCapturing(a.stream, &cap); e != hipSuccess) return e;
-    const bool concurrent = cap == hipStreamCaptureStatusNone && scan_blocks * 2 <= (unsigned)cus;
+    const bool concurrent = !a.in_order && cap == hipStreamCaptureStatusNone && scan_blocks * 2 <= (unsigned)cus;
     Pipeline pl;     // created only outside a capture
     if (concurrent)
         if (hipError_t e = pl.init(); e != hipSuccess) return e;

@@ -180,7 +180,9 @@ int kda_prefill(const void *q, const void *k, const void *v, const float *g,
  * of KDA_NOALLOC_SCRATCH_BYTES (128 MiB) in the library's device memory, one
  * per GPU, held from the library's first use on that GPU until the process
  * ends. Sizes whose workspace (kda_prefill_workspace_size) exceeds it return
- * KDA_ERR_WORKSPACE before anything is launched. The array is looked up on
+ * KDA_ERR_WORKSPACE before anything is launched. It creates no stream or
+ * event either: one long sequence runs its windows in order on `stream`.
+ * The array is looked up on
  * the device current at the call, and `stream` must belong to that device.
  * Every call on one GPU shares the array: calls that overlap in time on the
  * same GPU (different streams, or host threads without ordering) race and

@@ -1,7 +1,8 @@
 """kda_prefill_noalloc, called through the C ABI, against kda_prefill with a caller
 workspace: the same kernels run, so out and S_out must be bit-identical. Two calls
 in a row on the library's shared per-device array, the second smaller, then the
-fp32 path, then a size beyond the array (rejected before any launch)."""
+fp32 path, one long single sequence (windows run in order), then a size beyond the
+array (rejected before any launch)."""
 import ctypes
 
 import pytest
@@ -41,6 +42,16 @@ def test_noalloc_matches_kda_prefill_twice_then_smaller():
     _case(lib, inputs.prefill(8, 128, lengths=[300, 0, 129, 250], C=64, io="bf16", s0_std=0.2, seed=71))
     _case(lib, inputs.prefill(4, 128, lengths=[65, 1], C=64, io="bf16", s0_std=0.2, seed=72))
     _case(lib, inputs.prefill(2, 64, B=2, T=90, C=16, io="f32", s0_std=0.1, seed=73))
+
+
+def test_noalloc_long_single_sequence_in_order():
+    """One sequence of 2,055 chunks at H = 1: the windowed workspace (two windows of
+    records) fits the array; the windows run in order on the stream, bit-identical to
+    kda_prefill's overlapped run."""
+    lib = load_library()
+    T = 4 * 512 * 64 + 6 * 64 + 37
+    assert lib.kda_prefill_workspace_size(1, T, 1, 128, 128, 64, KDA_BF16) <= (128 << 20)
+    _case(lib, inputs.prefill(1, 128, B=1, T=T, C=64, io="bf16", s0_std=0.02, seed=74))
 
 
 def test_noalloc_rejects_sizes_beyond_its_array():
