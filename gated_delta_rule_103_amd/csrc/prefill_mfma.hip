@@ -415,6 +415,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     // masked entries may hold inf / nan: select, do not scale
                     if (lower) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
                     sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
+                    // the diagonal is d_t = q_t . k_t: (q_t E_t)(k_t / E_t) in fp32
+                    if (sc == tr) sDg[tr] = accM[i];
                 }
             }
             // Kr = k F H for the block's 16 tokens, written channel-major (Kr^T) so that
@@ -452,21 +454,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
                     }
                 }
-            }
-            // exact diagonal d_t = q_t . k_t (4 lanes per row, 32 channels each)
-            {
-                const int row = tid >> 2, seg = tid & 3;
-                float acc = 0.f;
-#pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const bf16x8 qa = lds8(sQ + row * SQ + 32 * seg + 8 * hh), ka = lds8(sK + row * SQ + 32 * seg + 8 * hh);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc += bf2f(qa[e]) * bf2f(ka[e]);
-                }
-                acc += __shfl_xor(acc, 1, 64);
-                acc += __shfl_xor(acc, 2, 64);
-                if constexpr (NORM) acc *= sRQ[row] * sRK[row];
-                if (seg == 0) sDg[row] = acc;
             }
         } else {
             // the wavefront's blocks (I, J0) and, when NB = 2, (I, 1), with the block
@@ -534,8 +521,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         for (int I = 0; I < 4 && (flags.x | flags.y | flags.z | flags.w); ++I) {
             if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) continue;   // uniform
             if (wave == I) {
-                for (int tr = 1; tr < 16; ++tr)
-                    for (int sc = 0; sc < tr; ++sc) {
+                // strictly lower L and Mqk, and the diagonal d_t (sc == tr: no decay)
+                for (int tr = 0; tr < 16; ++tr)
+                    for (int sc = 0; sc <= tr; ++sc) {
                         const int T_ = 16 * I + tr, S_ = 16 * I + sc;
                         float accl = 0.f, accm = 0.f;
                         for (int c = lane; c < D; c += 64) {
@@ -553,8 +541,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                             accm *= sRQ[T_] * sRK[S_];
                         }
                         if (lane == 0) {
-                            sLI[T_ * SL + S_] = sBeta[T_] * accl;
-                            sMqk[T_ * SMQ + S_] = static_cast<_Float16>(accm);
+                            if (sc < tr) {
+                                sLI[T_ * SL + S_] = sBeta[T_] * accl;
+                                sMqk[T_ * SMQ + S_] = static_cast<_Float16>(accm);
+                            } else {
+                                sDg[T_] = accm;
+                            }
                         }
                     }
                 for (int e = lane; e < 256; e += 64)
