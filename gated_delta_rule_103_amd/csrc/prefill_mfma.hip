@@ -143,17 +143,22 @@ constexpr int SL = C + 4;        // fp32 row stride of L / INV^T      [64][68]
 constexpr int SMQ = C + 8;       // fp16 row stride of Mqk            [64][72]
 constexpr int SKR = C + 8;       // fp16 row stride of Kr^T           [128][72]
 
+// The decayed operand tiles, formed once per item (fp32 [64][SE], the L2 norm
+// of q and k applied when requested): KE = k E and QE = q E (E: the in-block
+// prefix decay, block start -> token), KF = k F (F: the in-block suffix decay,
+// token -> block end). Every operand of the products is one of them times at
+// most one per-channel factor.
 struct PrepLds {
-    static constexpr int Q = 0;
-    static constexpr int K = Q + C * SQ * 2;
-    static constexpr int E = K + C * SQ * 2;         // fp32 in-block prefix decay
-    static constexpr int F = E + C * SE * 4;         // fp32 in-block suffix decay
-    static constexpr int LI = F + C * SE * 4;        // fp32 L (strictly lower) and INV^T (upper, with diagonal)
+    static constexpr int KE = 0;
+    static constexpr int QE = KE + C * SE * 4;
+    static constexpr int KF = QE + C * SE * 4;
+    static constexpr int LI = KF + C * SE * 4;       // fp32 L (strictly lower) and INV^T (upper, with diagonal)
     static constexpr int MQK = LI + C * SL * 4;      // fp16 strictly lower Mqk
     static constexpr int DG = MQK + C * SMQ * 2;     // fp32 [64]
     static constexpr int BETA = DG + C * 4;          // fp32 [64]
-    static constexpr int GB = BETA + C * 4;          // fp32 [4][128] block decays
-    static constexpr int G = GB + 4 * D * 4;         // fp32 [4][128] decay chunk start -> block start
+    static constexpr int GB = BETA + C * 4;          // fp32 [4][128] block decays Gamma
+    static constexpr int IGB = GB + 4 * D * 4;       // fp32 [4][128] 1 / Gamma (used where Gamma >= FLT_MIN)
+    static constexpr int G = IGB + 4 * D * 4;        // fp32 [4][128] decay chunk start -> block start
     static constexpr int GAM = G + 4 * D * 4;        // fp32 [128]
     static constexpr int RQ = GAM + D * 4;           // fp32 [64] 1 / ||q_t|| (L2-normalised input)
     static constexpr int RK = RQ + C * 4;            // fp32 [64] 1 / ||k_t||
@@ -161,7 +166,11 @@ struct PrepLds {
     static constexpr int T3 = FLAG + 16;             // fp32 [4][256] inverse scratch
     static constexpr int KRT = T3 + 4 * 256 * 4;     // fp16 [128][SKR] Kr^T, channel-major
     static constexpr int SIZE = KRT + D * SKR * 2;
+    // the bf16 rows of q and k are staged in the L and Kr^T tiles, free until the
+    // decayed tiles have been formed
+    static constexpr int QS = LI, KS = KRT;
 };
+static_assert(C * SQ * 2 <= C * SL * 4 && C * SQ * 2 <= D * SKR * 2, "q, k staging");
 
 struct PrepParams {
     const bf16_t *q, *k;
@@ -188,22 +197,24 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(SeqView sv, int2 *meta,
 
 // GHEAD: one log-decay per (token, head), g [T][H] or none (nullptr), instead
 // of one per key channel. NORM: q and k are L2-normalised over the channels on
-// the fly: the staged rows stay the bf16 inputs, and 1/||q_t||, 1/||k_t|| (fp32)
-// scale every product they enter before its operands are rounded.
+// the fly: 1/||q_t||, 1/||k_t|| (fp32, from the staged bf16 rows) scale the
+// decayed tiles as they are formed.
 template <typename TB, bool VARLEN, bool GHEAD, bool NORM>
 __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
     static_assert(Lo::SIZE <= 163840, "LDS budget");
-    __bf16 *sQ = reinterpret_cast<__bf16 *>(smem + Lo::Q);
-    __bf16 *sK = reinterpret_cast<__bf16 *>(smem + Lo::K);
-    float *sE = reinterpret_cast<float *>(smem + Lo::E);
-    float *sF = reinterpret_cast<float *>(smem + Lo::F);
+    __bf16 *sQs = reinterpret_cast<__bf16 *>(smem + Lo::QS);
+    __bf16 *sKs = reinterpret_cast<__bf16 *>(smem + Lo::KS);
+    float *sKE = reinterpret_cast<float *>(smem + Lo::KE);
+    float *sQE = reinterpret_cast<float *>(smem + Lo::QE);
+    float *sKF = reinterpret_cast<float *>(smem + Lo::KF);
     float *sLI = reinterpret_cast<float *>(smem + Lo::LI);
     _Float16 *sMqk = reinterpret_cast<_Float16 *>(smem + Lo::MQK);
     float *sDg = reinterpret_cast<float *>(smem + Lo::DG);
     float *sBeta = reinterpret_cast<float *>(smem + Lo::BETA);
     float *sGB = reinterpret_cast<float *>(smem + Lo::GB);
+    float *sIGB = reinterpret_cast<float *>(smem + Lo::IGB);
     float *sG = reinterpret_cast<float *>(smem + Lo::G);
     float *sGam = reinterpret_cast<float *>(smem + Lo::GAM);
     float *sRQ = reinterpret_cast<float *>(smem + Lo::RQ);
@@ -211,9 +222,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
     float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
     _Float16 *sKrt = reinterpret_cast<_Float16 *>(smem + Lo::KRT);
-    // Kd^T [128][SKR] fp16, channel-major, built over the F tile once F is dead
-    _Float16 *sKdT = reinterpret_cast<_Float16 *>(smem + Lo::F);
-    static_assert(D * SKR * 2 <= C * SE * 4, "Kd^T fits over the F tile");
+    // Kd^T [128][SKR] fp16, channel-major, built over the KF tile once it is dead
+    _Float16 *sKdT = reinterpret_cast<_Float16 *>(smem + Lo::KF);
+    static_assert(D * SKR * 2 <= C * SE * 4, "Kd^T fits over the KF tile");
 
     const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // 8 wavefronts
     const int H = p.H;
@@ -309,13 +320,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
 
-        // ================= stage the chunk in LDS (rows past the end: zeros, alpha = 1)
+        // ================= stage q and k in LDS (rows past the end: zeros, alpha = 1)
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int idx = tid + it * PTHR, row = idx >> 4, part = idx & 15;
             const u32x4 z0 = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(sQ + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
-            *reinterpret_cast<u32x4 *>(sK + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
+            *reinterpret_cast<u32x4 *>(sQs + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
+            *reinterpret_cast<u32x4 *>(sKs + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
             if constexpr (NORM) {
                 // sums of squares over the 16 threads of the row (lanes 16j..16j+15)
                 const bf16x8 qx = __builtin_bit_cast(bf16x8, rq[it]), kx = __builtin_bit_cast(bf16x8, rk[it]);
@@ -337,26 +348,28 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         // in-block suffix (F) and prefix (E) products of alpha = exp(g), one
-        // (block, channel) per thread, from the registers (rows past the end: alpha = 1)
+        // (block, channel) per thread, kept in registers (rows past the end: alpha = 1)
+        const int bI = tid >> 7, bc = tid & 127;
+        float ev[16], fv[16];
         {
-            const int I = tid >> 7, c = tid & 127;
             float al[16];
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) al[tt] = 16 * I + tt < Lc ? __expf(rg[tt]) : 1.f;
+            for (int tt = 0; tt < 16; ++tt) al[tt] = 16 * bI + tt < Lc ? __expf(rg[tt]) : 1.f;
             float f = 1.f;
 #pragma unroll
             for (int tt = 15; tt >= 0; --tt) {
-                sF[(16 * I + tt) * SE + c] = f;
+                fv[tt] = f;
                 f *= al[tt];
             }
             float e = 1.f;
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt) {
                 e *= al[tt];
-                sE[(16 * I + tt) * SE + c] = e;
+                ev[tt] = e;
             }
-            sGB[I * D + c] = e;
-            if (!(e >= kTiny)) atomicOr(&sFlag[I], 1);     // flags were cleared during the previous item
+            sGB[bI * D + bc] = e;
+            sIGB[bI * D + bc] = __builtin_amdgcn_rcpf(e);     // read only for blocks with e >= FLT_MIN
+            if (!(e >= kTiny)) atomicOr(&sFlag[bI], 1);     // flags were cleared during the previous item
         }
         if (tid < C) sBeta[tid] = tid < Lc ? ld_scalar<TB>(&rbeta, 0) : 0.f;
         __syncthreads();
@@ -369,15 +382,27 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             sG[c] = 1.f; sG[D + c] = g0; sG[2 * D + c] = g0 * g1; sG[3 * D + c] = g0 * g1 * g2;
             sGam[c] = g0 * g1 * g2 * g3;
         }
+        // the decayed tiles KE, QE, KF: thread (block, channel) forms its 16 rows
+        // from the decays in its registers
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+            const int t = 16 * bI + tt;
+            const float kk = NORM ? bf2f(sKs[t * SQ + bc]) * sRK[t] : bf2f(sKs[t * SQ + bc]);
+            const float qq = NORM ? bf2f(sQs[t * SQ + bc]) * sRQ[t] : bf2f(sQs[t * SQ + bc]);
+            sKE[t * SE + bc] = kk * ev[tt];
+            sQE[t * SE + bc] = qq * ev[tt];
+            sKF[t * SE + bc] = kk * fv[tt];
+        }
+        __syncthreads();
 
         // ================= L and Mqk on MFMA, the 10 16x16 blocks with I >= J
-        // Left operands x_t E_t (x = k for L, q for Mqk), t in block I.
-        // Diagonal blocks (wavefronts 0-3, I = J = wavefront): right operands k_s / E_s
-        // (start of block as reference, bounded by 1 / Gamma_I; a block with Gamma_I
-        // below FLT_MIN takes the exact path instead), multiplied in fp32 on
-        // v_mfma_f32_16x16x4f32: near-diagonal entries dominate o, and fp32
-        // operands need no hi/lo splitting on the vector ALU.
-        // Off-diagonal blocks (wavefronts 4-7): right operands k_s F_s
+        // Left operands x_t E_t (KE for L, QE for Mqk), t in block I.
+        // Diagonal blocks (wavefronts 0-3, I = J = wavefront): right operands
+        // k_s / E_s = KF_s / Gamma_I (start of block as reference, bounded by
+        // 1 / Gamma_I; a block with Gamma_I below FLT_MIN takes the exact path
+        // instead), multiplied in fp32 on v_mfma_f32_16x16x4f32: near-diagonal
+        // entries dominate o, and fp32 operands need no hi/lo splitting.
+        // Off-diagonal blocks (wavefronts 4-7): right operands KF_s
         // prod_{J<K<I} Gamma_K; every factor is <= 1, so both operands are rounded
         // once to fp16 (11-bit significand) and multiplied on fp16 MFMA. A wave's
         // blocks share their row block, so its left operands are built once.
@@ -388,26 +413,29 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const int I = wave;
             if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) {
                 const int t = 16 * I + l16;
-                const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
-                f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
+                // two partial sums per product (even and odd k-slots), so that four
+                // independent MFMA chains fill the pipe
+                f32x4 aL[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, aM[2] = {aL[0], aL[0]};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     // lane: row / column t, channels 32ks + 8lq + e; product e contracts
                     // channels 32ks + 8j + e over the four k-slots j
                     const int c0 = 32 * ks + 8 * lq;
-                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
-                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    f32x4 ke[2], qe[2], bk[2];
+#pragma unroll
+                    for (int hv = 0; hv < 2; ++hv) {
+                        ke[hv] = *reinterpret_cast<const f32x4 *>(sKE + t * SE + c0 + 4 * hv);
+                        qe[hv] = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0 + 4 * hv);
+                        bk[hv] = *reinterpret_cast<const f32x4 *>(sKF + t * SE + c0 + 4 * hv) *
+                                 *reinterpret_cast<const f32x4 *>(sIGB + I * D + c0 + 4 * hv);
+                    }
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float ee = e < 4 ? e0[e] : e1[e - 4];
-                        const float kk = NORM ? bf2f(kv[e]) * nk : bf2f(kv[e]);
-                        const float qq = NORM ? bf2f(qv[e]) * nq : bf2f(qv[e]);
-                        const float bk = kk * __builtin_amdgcn_rcpf(ee);
-                        accL = __builtin_amdgcn_mfma_f32_16x16x4f32(kk * ee, bk, accL, 0, 0, 0);
-                        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(qq * ee, bk, accM, 0, 0, 0);
+                        aL[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(ke[e >> 2][e & 3], bk[e >> 2][e & 3], aL[e & 1], 0, 0, 0);
+                        aM[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qe[e >> 2][e & 3], bk[e >> 2][e & 3], aM[e & 1], 0, 0, 0);
                     }
                 }
+                const f32x4 accL = aL[0] + aL[1], accM = aM[0] + aM[1];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
@@ -415,19 +443,17 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     // masked entries may hold inf / nan: select, do not scale
                     if (lower) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
                     sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
-                    // the diagonal is d_t = q_t . k_t: (q_t E_t)(k_t / E_t) in fp32
+                    // the diagonal is d_t = q_t . k_t: (q_t E_t)(k_t F_t / Gamma_I) in fp32
                     if (sc == tr) sDg[tr] = accM[i];
                 }
             }
-            // Kr = k F H for the block's 16 tokens, written channel-major (Kr^T) so that
+            // Kr = KF H for the block's 16 tokens, written channel-major (Kr^T) so that
             // the record's Kr^T fragments are single 16-byte reads. This wave is
             // otherwise idle until the off-diagonal blocks are done. A lane takes a
             // token pair (16I + 2(lane & 7), +1) and eight-channel groups lane >> 3 and
             // (lane >> 3) + 8, and writes each (channel, token pair) as one dword.
             {
                 const int t0 = 16 * I + 2 * (lane & 7);
-                float nk0 = 1.f, nk1 = 1.f;
-                if constexpr (NORM) { nk0 = sRK[t0]; nk1 = sRK[t0 + 1]; }
 #pragma unroll
                 for (int gg = 0; gg < 2; ++gg) {
                     const int c0 = 8 * ((lane >> 3) + 8 * gg);
@@ -439,16 +465,15 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                             h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
                             h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
                         }
-                    const bf16x8 ka = lds8(sK + t0 * SQ + c0), kb = lds8(sK + (t0 + 1) * SQ + c0);
-                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sF + t0 * SE + c0);
-                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sF + t0 * SE + c0 + 4);
-                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sF + (t0 + 1) * SE + c0);
-                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sF + (t0 + 1) * SE + c0 + 4);
+                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0);
+                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0 + 4);
+                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0);
+                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0 + 4);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float hh = e < 4 ? h0[e] : h1[e - 4];
-                        const float xa = bf2f(ka[e]) * nk0 * (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
-                        const float xb = bf2f(kb[e]) * nk1 * (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
+                        const float xa = (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
+                        const float xb = (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
                         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
                         const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
                         *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
@@ -465,37 +490,33 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int bb = 0; bb < NB; ++bb) { accL[bb] = f32x4{0.f, 0.f, 0.f, 0.f}; accM[bb] = accL[bb]; }
                 const int t = 16 * I + l16;
-                const float nq = NORM ? sRQ[t] : 1.f, nk = NORM ? sRK[t] : 1.f;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c0 = 32 * ks + 8 * lq;
-                    const bf16x8 qv = lds8(sQ + t * SQ + c0), kv = lds8(sK + t * SQ + c0);
-                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
-                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0 + 4);
+                    const f32x4 ka0 = *reinterpret_cast<const f32x4 *>(sKE + t * SE + c0);
+                    const f32x4 ka1 = *reinterpret_cast<const f32x4 *>(sKE + t * SE + c0 + 4);
+                    const f32x4 qa0 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
+                    const f32x4 qa1 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0 + 4);
                     f16x8 aq, ak;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float fa = e < 4 ? a0[e] : a1[e - 4];
-                        aq[e] = static_cast<_Float16>(NORM ? bf2f(qv[e]) * nq * fa : bf2f(qv[e]) * fa);
-                        ak[e] = static_cast<_Float16>(NORM ? bf2f(kv[e]) * nk * fa : bf2f(kv[e]) * fa);
+                        aq[e] = static_cast<_Float16>(e < 4 ? qa0[e] : qa1[e - 4]);
+                        ak[e] = static_cast<_Float16>(e < 4 ? ka0[e] : ka1[e - 4]);
                     }
 #pragma unroll
                     for (int bb = 0; bb < NB; ++bb) {
                         const int J = bb ? 1 : J0, sr = 16 * J + l16;
-                        const bf16x8 sv = lds8(sK + sr * SQ + c0);
-                        f32x4 b0 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0);
-                        f32x4 b1 = *reinterpret_cast<const f32x4 *>(sF + sr * SE + c0 + 4);
+                        f32x4 b0 = *reinterpret_cast<const f32x4 *>(sKF + sr * SE + c0);
+                        f32x4 b1 = *reinterpret_cast<const f32x4 *>(sKF + sr * SE + c0 + 4);
                         // prod_{J<K<I} Gamma_K (none for adjacent blocks)
 #pragma unroll
                         for (int K = J + 1; K < I; ++K) {
                             b0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
                             b1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
                         }
-                        const float ns = NORM ? sRK[sr] : 1.f;
                         f16x8 bk;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            bk[e] = static_cast<_Float16>((NORM ? bf2f(sv[e]) * ns : bf2f(sv[e])) * (e < 4 ? b0[e] : b1[e - 4]));
+                        for (int e = 0; e < 8; ++e) bk[e] = static_cast<_Float16>(e < 4 ? b0[e] : b1[e - 4]);
                         accL[bb] = mfma_f16(ak, bk, accL[bb]);
                         accM[bb] = mfma_f16(aq, bk, accM[bb]);
                     }
@@ -526,13 +547,19 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     for (int sc = 0; sc <= tr; ++sc) {
                         const int T_ = 16 * I + tr, S_ = 16 * I + sc;
                         float accl = 0.f, accm = 0.f;
+                        // raw q and k from memory (the tiles hold them decayed); rows past
+                        // the end count as zeros (their loads read the last row)
+                        const size_t rT = ((size_t)(tok0 + min(T_, Lc - 1)) * H + h) * D;
+                        const size_t rS = ((size_t)(tok0 + min(S_, Lc - 1)) * H + h) * D;
+                        const float mT = T_ < Lc ? 1.f : 0.f, mS = S_ < Lc ? 1.f : 0.f;
                         for (int c = lane; c < D; c += 64) {
                             float lg = 0.f;
                             for (int rho = S_ + 1; rho <= T_; ++rho)
                                 if (rho < Lc) lg += GateRow(p.g, GHEAD, (size_t)(tok0 + rho) * H + h, D).at(c);
-                            const float w = expf(lg), kk = bf2f(sK[S_ * SQ + c]);
-                            accl += bf2f(sK[T_ * SQ + c]) * kk * w;
-                            accm += bf2f(sQ[T_ * SQ + c]) * kk * w;
+                            const float w = expf(lg);
+                            const float kk = mS * bf16_to_f32(p.k[rS + c]);
+                            accl += mT * bf16_to_f32(p.k[rT + c]) * kk * w;
+                            accm += mT * bf16_to_f32(p.q[rT + c]) * kk * w;
                         }
                         accl = warp_sum(accl);
                         accm = warp_sum(accm);
@@ -583,54 +610,47 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
         } else if (wave >= 4) {
             const int tt = wave & 3;
-            // Kd^T = (k e^{a})^T, channel-major: a lane takes a token pair (16 tt +
-            // 2 (lane & 7), +1) and eight-channel groups lane >> 3 and (lane >> 3) + 8,
-            // and writes each (channel, token pair) as one dword. The chunk-start
-            // decay of token t is G (chunk start -> block start) times E (block
-            // start -> t).
+            // Kd^T = (k e^{a})^T = (KE G)^T, channel-major: a lane takes a token pair
+            // (16 tt + 2 (lane & 7), +1) and eight-channel groups lane >> 3 and
+            // (lane >> 3) + 8, and writes each (channel, token pair) as one dword.
+            // The chunk-start decay of token t is G (chunk start -> block start)
+            // times E (block start -> t).
             {
                 const int t0 = 16 * tt + 2 * (lane & 7);
-                float nk0 = 1.f, nk1 = 1.f;
-                if constexpr (NORM) { nk0 = sRK[t0]; nk1 = sRK[t0 + 1]; }
 #pragma unroll
                 for (int gg = 0; gg < 2; ++gg) {
                     const int c0 = 8 * ((lane >> 3) + 8 * gg);
                     const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
                     const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0 + 4);
-                    const bf16x8 ka = lds8(sK + t0 * SQ + c0), kb = lds8(sK + (t0 + 1) * SQ + c0);
-                    const f32x4 ea0 = *reinterpret_cast<const f32x4 *>(sE + t0 * SE + c0);
-                    const f32x4 ea1 = *reinterpret_cast<const f32x4 *>(sE + t0 * SE + c0 + 4);
-                    const f32x4 eb0 = *reinterpret_cast<const f32x4 *>(sE + (t0 + 1) * SE + c0);
-                    const f32x4 eb1 = *reinterpret_cast<const f32x4 *>(sE + (t0 + 1) * SE + c0 + 4);
+                    const f32x4 ea0 = *reinterpret_cast<const f32x4 *>(sKE + t0 * SE + c0);
+                    const f32x4 ea1 = *reinterpret_cast<const f32x4 *>(sKE + t0 * SE + c0 + 4);
+                    const f32x4 eb0 = *reinterpret_cast<const f32x4 *>(sKE + (t0 + 1) * SE + c0);
+                    const f32x4 eb1 = *reinterpret_cast<const f32x4 *>(sKE + (t0 + 1) * SE + c0 + 4);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float gg_ = e < 4 ? g0[e] : g1[e - 4];
-                        const float xa = bf2f(ka[e]) * nk0 * (e < 4 ? ea0[e] : ea1[e - 4]) * gg_;
-                        const float xb = bf2f(kb[e]) * nk1 * (e < 4 ? eb0[e] : eb1[e - 4]) * gg_;
+                        const float xa = (e < 4 ? ea0[e] : ea1[e - 4]) * gg_;
+                        const float xb = (e < 4 ? eb0[e] : eb1[e - 4]) * gg_;
                         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
                         const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
                         *reinterpret_cast<f16x2 *>(sKdT + (c0 + e) * SKR + t0) = pr;
                     }
                 }
             }
-            // Qd = q e^{a} for token tile tt, one fragment per scan wavefront w, in
-            // that wavefront's state-channel order (channels 32w + 4lq + {0..3},
+            // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
+            // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
             // 32w + 16 + 4lq + {0..3})
             {
                 const int t = 16 * tt + l16;
-                const float nr = NORM ? sRQ[t] : 1.f;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
                         const int c0 = 32 * w + 16 * hh + 4 * lq;
-                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(sQ + t * SQ + c0);
-                        const f32x4 e4 = *reinterpret_cast<const f32x4 *>(sE + t * SE + c0);
+                        const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
                         const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            fr[w][4 * hh + i] = static_cast<_Float16>(bf2f(xv[i]) * nr * (g4[i] * e4[i]));
+                        for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
                     }
             }
             // strictly lower Mqk for token tile tt in the scan's token order of U
