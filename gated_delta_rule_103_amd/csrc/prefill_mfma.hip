@@ -591,24 +591,38 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // every later row at once, so the updates of a step are independent and the
         // L column reads (wave-uniform addresses) do not wait on the arithmetic.
         // Entries above the diagonal stay 0 (they only ever see x[sc] = 0).
-        // Meanwhile waves 4-7 (token tile tt = wave - 4), idle until the record,
-        // build what does not depend on the inverse: Kd^T for the W product (into
-        // LDS, over the F tile, which is dead now), and their tile's Qd and Mqk
-        // fragments, held in registers until the record is stored.
+        // Waves 0-3 also take their Kr^T record fragments, and waves 4-7 (token
+        // tile tt = wave - 4) build Kd^T for the W product (into LDS, over the F
+        // tile, which is dead now). Every record fragment is held in registers
+        // until the record is stored.
         f16x8 fr[8];
-        if (wave < 4 && lane < 16) {
-            const int I = wave, col = lane;
-            float x[16];
+        if (wave < 4) {
+            if (lane < 16) {
+                const int I = wave, col = lane;
+                float x[16];
 #pragma unroll
-            for (int tr = 0; tr < 16; ++tr) x[tr] = (tr == col) ? 1.f : 0.f;
+                for (int tr = 0; tr < 16; ++tr) x[tr] = (tr == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int sc = 0; sc < 15; ++sc)
+                for (int sc = 0; sc < 15; ++sc)
 #pragma unroll
-                for (int tr = sc + 1; tr < 16; ++tr) x[tr] -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
+                    for (int tr = sc + 1; tr < 16; ++tr) x[tr] -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
 #pragma unroll
-            for (int tr = 0; tr < 16; ++tr)
-                if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
-        } else if (wave >= 4) {
+                for (int tr = 0; tr < 16; ++tr)
+                    if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
+            }
+            // Kr^T record fragments: rows = channels 32w + 16rt + l16, k = tokens of
+            // U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); Kr^T is final
+            typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const _Float16 *row = sKrt + (32 * wave + 16 * rt + l16) * SKR + 32 * ks + 4 * lq;
+                    const f16x4_ a = *reinterpret_cast<const f16x4_ *>(row);
+                    const f16x4_ b = *reinterpret_cast<const f16x4_ *>(row + 16);
+                    fr[2 * rt + ks] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+                }
+        } else {
             const int tt = wave & 3;
             // Kd^T = (k e^{a})^T = (KE G)^T, channel-major: a lane takes a token pair
             // (16 tt + 2 (lane & 7), +1) and eight-channel groups lane >> 3 and
@@ -636,39 +650,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         *reinterpret_cast<f16x2 *>(sKdT + (c0 + e) * SKR + t0) = pr;
                     }
                 }
-            }
-            // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
-            // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
-            // 32w + 16 + 4lq + {0..3})
-            {
-                const int t = 16 * tt + l16;
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int c0 = 32 * w + 16 * hh + 4 * lq;
-                        const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
-                        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
-                    }
-            }
-            // strictly lower Mqk for token tile tt in the scan's token order of U
-            // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
-            // the diagonal block are never written and are selected as zeros (a
-            // select, so stale LDS contents cannot leak in)
-            {
-                const int t = 16 * tt + l16;
-                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
-                        const bool zero = 2 * ks + hh > tt;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
-                    }
             }
         }
         __syncthreads();
@@ -709,6 +690,26 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -O4[i];
+            } else if (wave >= 4) {
+                // waves 4-7 (token tile tt), idle in the inverse stages, build their
+                // Qd and Mqk record fragments here
+                const int tt = wave & 3;
+                // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
+                // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
+                // 32w + 16 + 4lq + {0..3})
+                {
+                    const int t = 16 * tt + l16;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int c0 = 32 * w + 16 * hh + 4 * lq;
+                            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
+                            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
+                        }
+                }
             }
             __syncthreads();
             // stage 2a: wave w < 4 takes P_IJ with I = 2 + (w >> 1), J = w & 1
@@ -726,6 +727,25 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 float *pw = sT3 + wave * 256;                   // P_IJ, [row][col]
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pw[(4 * lq + i) * 16 + l16] = P4[i];
+            } else {
+                const int tt = wave & 3;
+                // strictly lower Mqk for token tile tt in the scan's token order of U
+                // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
+                // the diagonal block are never written and are selected as zeros (a
+                // select, so stale LDS contents cannot leak in)
+                {
+                    const int t = 16 * tt + l16;
+                    typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
+                            const bool zero = 2 * ks + hh > tt;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
+                        }
+                }
             }
             __syncthreads();
             // stage 2b: wave w < 4 takes INV_IJ with I = 2 + (w >> 1), J = w & 1
@@ -774,18 +794,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 }
             }
             if (wave < 4) {
-                // Kr^T fragments: rows = channels 32w + 16rt + l16, k = tokens of U's
-                // order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3})
-                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const _Float16 *row = sKrt + (32 * wave + 16 * rt + l16) * SKR + 32 * ks + 4 * lq;
-                        const f16x4_ a = *reinterpret_cast<const f16x4_ *>(row);
-                        const f16x4_ b = *reinterpret_cast<const f16x4_ *>(row + 16);
-                        fr[2 * rt + ks] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-                    }
                 fr[4] = ib[0];
                 fr[5] = ib[1];
             }
