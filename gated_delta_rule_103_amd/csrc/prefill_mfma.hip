@@ -163,8 +163,7 @@ struct PrepLds {
     static constexpr int RQ = GAM + D * 4;           // fp32 [64] 1 / ||q_t|| (L2-normalised input)
     static constexpr int RK = RQ + C * 4;            // fp32 [64] 1 / ||k_t||
     static constexpr int FLAG = RK + C * 4;          // int [4]
-    static constexpr int T3 = FLAG + 16;             // fp32 [4][256] inverse scratch
-    static constexpr int KRT = T3 + 4 * 256 * 4;     // fp16 [128][SKR] Kr^T, channel-major
+    static constexpr int KRT = FLAG + 16;            // fp16 [128][SKR] Kr^T, channel-major
     static constexpr int SIZE = KRT + D * SKR * 2;
     // the bf16 rows of q and k are staged in the L and Kr^T tiles, free until the
     // decayed tiles have been formed
@@ -220,7 +219,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     float *sRQ = reinterpret_cast<float *>(smem + Lo::RQ);
     float *sRK = reinterpret_cast<float *>(smem + Lo::RK);
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
-    float *sT3 = reinterpret_cast<float *>(smem + Lo::T3);
     _Float16 *sKrt = reinterpret_cast<_Float16 *>(smem + Lo::KRT);
     // Kd^T [128][SKR] fp16, channel-major, built over the KF tile once it is dead
     _Float16 *sKdT = reinterpret_cast<_Float16 *>(smem + Lo::KF);
@@ -654,117 +652,122 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         }
         __syncthreads();
         fetch(next, 2);
-        // off-diagonal blocks on fp32 MFMA (exact products), with the 64 x 64 inverse
-        // taken as 2 x 2 blocks of 32 (A, D its diagonal halves, C = L[32:64][0:32]):
-        //   stage 1:  INV_10 = -INV_11 L_10 INV_00,  INV_32 = -INV_33 L_32 INV_22
-        //   stage 2a: P = C A^{-1}    (P_IJ = sum_{J<=K<=1} L_IK INV_KJ, I in {2,3}, J in {0,1})
-        //   stage 2b: INV_IJ = -sum_{2<=K<=I} INV_IK P_KJ
-        // Four dependent products on the critical path instead of six for three
-        // levels of INV_IJ = -INV_II sum_K L_IK INV_KJ. Operands: a 16x16x4 fragment
-        // gives lane (l16, lq) A[row = l16][k] and B[k][col = l16], k = 4 sl + lq.
-        // INV_XY[a][b] lives at sLI[(16Y + b) * SL + 16X + a]; for X == Y only a >= b is stored.
-        {
-            const int row = l16, kk = lq;
-            // INV_XY[r][c] (X >= Y, zero above the diagonal of a diagonal block)
-            auto inv_at = [&](int X, int Y, int r, int c) {
-                return (X == Y && c > r) ? 0.f : sLI[(16 * Y + c) * SL + 16 * X + r];
+        // off-diagonal blocks of INV on fp32 MFMA (exact products). With the 64 x 64
+        // inverse taken as 2 x 2 blocks of 32 (A, D its diagonal halves, C its
+        // lower-left block), INV = [[A^-1, 0], [-D^-1 C A^-1, D^-1]]:
+        //   INV_10 = -INV_11 L_10 INV_00,  INV_32 = -INV_33 L_32 INV_22
+        //   P_IJ = sum_{J<=K<=1} L_IK INV_KJ      (P = C A^-1; I in {2,3}, J in {0,1})
+        //   INV_IJ = -sum_{2<=K<=I} INV_IK P_KJ
+        // Wavefront w < 4 forms one of INV_20, INV_21, INV_30, INV_31 on its own,
+        // with no barrier: what it needs of the others' blocks (INV_10, INV_32, P_2J)
+        // it forms again itself, and every intermediate product stays in registers.
+        // A 16x16x4 fragment in step sl takes A[row = l16][k] and B[k][col = l16]
+        // from lane (l16, lq) with k = 4 lq + sl (the order of k inside a product is
+        // free) and leaves C[4 lq + i][l16] there, so a product held in that layout
+        // is the right operand of the next one as it stands (element sl), and the
+        // transpose of such a product is a left operand. Most operands are then one
+        // 16-byte LDS read: the rows of L, and the rows of INV^T (INV_XY[a][b]
+        // lives at sLI[(16Y + b) * SL + 16X + a]; for X == Y only a >= b is stored,
+        // the rest is selected as zero).
+        if (wave < 4) {
+            auto mm = [](f32x4 acc, f32x4 a, f32x4 b) {
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[sl], b[sl], acc, 0, 0, 0);
+                return acc;
             };
-            if (wave < 2) {                                     // stage 1
-                const int J = 2 * wave, I = J + 1;
-                f32x4 T4 = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            const int k0 = 4 * lq;
+            // L_XY[l16][k] (row-major)
+            auto l_rk = [&](int X, int Y) { return *reinterpret_cast<const f32x4 *>(sLI + (16 * X + l16) * SL + 16 * Y + k0); };
+            // INV_XX[k][l16], which is also INV_XX^T[l16][k]
+            auto inv_kc = [&](int X) {
+                f32x4 v = *reinterpret_cast<const f32x4 *>(sLI + (16 * X + l16) * SL + 16 * X + k0);
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) v[sl] = k0 + sl < l16 ? 0.f : v[sl];
+                return v;
+            };
+            // INV_XX[l16][k]
+            auto inv_rk = [&](int X) {
+                f32x4 v;
 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {
-                    const int k = 4 * sl + kk;
-                    T4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sLI[(16 * I + row) * SL + 16 * J + k],   // L_IJ[row][k]
-                                                              inv_at(J, J, k, row), T4, 0, 0, 0);      // INV_JJ[k][col]
+                    const float x = sLI[(16 * X + k0 + sl) * SL + 16 * X + l16];
+                    v[sl] = k0 + sl > l16 ? 0.f : x;
                 }
-                float *tw = sT3 + wave * 256;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tw[(4 * lq + i) * 16 + l16] = T4[i];
-                __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): scratch written before it is read
-                f32x4 O4 = {0.f, 0.f, 0.f, 0.f};
+                return v;
+            };
+            const int I = 2 + (wave >> 1), J = wave & 1;        // this wavefront's INV_IJ
+            f32x4 inv10 = z4, inv32t = z4;
+            if (J == 0)                                         // INV_10 = -INV_11 (L_10 INV_00)
+                inv10 = -mm(z4, inv_rk(1), mm(z4, l_rk(1, 0), inv_kc(0)));
+            if (I == 3) {                                       // INV_32^T = -INV_22^T (L_32^T INV_33^T)
+                f32x4 a, b;                                     // L_32^T[l16][k], INV_33^T[k][l16]
 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {
-                    const int k = 4 * sl + kk;
-                    O4 = __builtin_amdgcn_mfma_f32_16x16x4f32(inv_at(I, I, row, k), tw[k * 16 + l16], O4, 0, 0, 0);
+                    a[sl] = sLI[(48 + k0 + sl) * SL + 32 + l16];
+                    const float x = sLI[(48 + k0 + sl) * SL + 48 + l16];
+                    b[sl] = k0 + sl > l16 ? 0.f : x;
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -O4[i];
-            } else if (wave >= 4) {
-                // waves 4-7 (token tile tt), idle in the inverse stages, build their
-                // Qd and Mqk record fragments here
-                const int tt = wave & 3;
-                // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
-                // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
-                // 32w + 16 + 4lq + {0..3})
-                {
-                    const int t = 16 * tt + l16;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-#pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) {
-                            const int c0 = 32 * w + 16 * hh + 4 * lq;
-                            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
-                            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
-                        }
-                }
+                inv32t = -mm(z4, inv_kc(2), mm(z4, a, b));
             }
-            __syncthreads();
-            // stage 2a: wave w < 4 takes P_IJ with I = 2 + (w >> 1), J = w & 1
-            if (wave < 4) {
-                const int I = 2 + (wave >> 1), J = wave & 1;
-                f32x4 P4 = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < 2; ++K) {
+            // P_XJ = L_XJ INV_JJ (+ L_X1 INV_10 when J == 0)
+            const f32x4 bJ = inv_kc(J);
+            auto p_of = [&](int X) {
+                f32x4 acc = mm(z4, l_rk(X, J), bJ);
+                if (J == 0) acc = mm(acc, l_rk(X, 1), inv10);
+                return acc;
+            };
+            const f32x4 p2 = p_of(2);
+            f32x4 o = mm(z4, inv_rk(I), I == 2 ? p2 : p_of(3));
+            if (I == 3) o = mm(o, inv32t, p2);
 #pragma unroll
-                    for (int sl = 0; sl < 4; ++sl) {
-                        const int k = 4 * sl + kk;
-                        P4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sLI[(16 * I + row) * SL + 16 * K + k],  // L_IK[row][k]
-                                                                  inv_at(K, J, k, row), P4, 0, 0, 0);     // INV_KJ[k][col]
+            for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -o[i];
+            // the blocks formed on the way that are stored once
+            if (wave == 0)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sLI[l16 * SL + 16 + 4 * lq + i] = inv10[i];          // INV_10
+            if (wave == 3)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sLI[(32 + 4 * lq + i) * SL + 48 + l16] = inv32t[i];  // INV_32
+        } else {
+            // waves 4-7 (token tile tt), idle here, build their Qd and Mqk record
+            // fragments
+            const int tt = wave & 3;
+            // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
+            // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
+            // 32w + 16 + 4lq + {0..3})
+            {
+                const int t = 16 * tt + l16;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int c0 = 32 * w + 16 * hh + 4 * lq;
+                        const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
+                        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
                     }
-                }
-                float *pw = sT3 + wave * 256;                   // P_IJ, [row][col]
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pw[(4 * lq + i) * 16 + l16] = P4[i];
-            } else {
-                const int tt = wave & 3;
-                // strictly lower Mqk for token tile tt in the scan's token order of U
-                // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
-                // the diagonal block are never written and are selected as zeros (a
-                // select, so stale LDS contents cannot leak in)
-                {
-                    const int t = 16 * tt + l16;
-                    typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) {
-                            const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
-                            const bool zero = 2 * ks + hh > tt;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
-                        }
-                }
             }
-            __syncthreads();
-            // stage 2b: wave w < 4 takes INV_IJ with I = 2 + (w >> 1), J = w & 1
-            if (wave < 4) {
-                const int I = 2 + (wave >> 1), J = wave & 1;
-                f32x4 O4 = {0.f, 0.f, 0.f, 0.f};
-                for (int K = 2; K <= I; ++K) {
-                    const float *pk = sT3 + ((K - 2) * 2 + J) * 256;    // P_KJ
+            // strictly lower Mqk for token tile tt in the scan's token order of U
+            // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
+            // the diagonal block are never written and are selected as zeros (a
+            // select, so stale LDS contents cannot leak in)
+            {
+                const int t = 16 * tt + l16;
+                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
 #pragma unroll
-                    for (int sl = 0; sl < 4; ++sl) {
-                        const int k = 4 * sl + kk;
-                        O4 = __builtin_amdgcn_mfma_f32_16x16x4f32(inv_at(I, K, row, k), pk[k * 16 + l16], O4, 0, 0, 0);
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
+                        const bool zero = 2 * ks + hh > tt;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
                     }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -O4[i];
             }
-            __syncthreads();
         }
+        __syncthreads();
 
         // ================= record: fp16 fragments of the scan's operands
         // Wavefront p: token tile tt = p & 3. Waves 0-3 (scan wavefront w = p)
