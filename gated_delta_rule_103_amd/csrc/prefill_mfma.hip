@@ -405,6 +405,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // once to fp16 (11-bit significand) and multiplied on fp16 MFMA. A wave's
         // blocks share their row block, so its left operands are built once.
         //   wavefront 4: (3,0) (3,1)   5: (3,2)   6: (2,0) (2,1)   7: (1,0)
+        // Then waves 4-7 form Kr^T of block wave - 4, and waves 0-3 invert their
+        // diagonal block of I + L.
         // the four flags in one LDS read (a serial read per block cost a round trip each)
         const int4 flags = *reinterpret_cast<const int4 *>(sFlag);
         if (wave < 4) {
@@ -443,39 +445,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
                     // the diagonal is d_t = q_t . k_t: (q_t E_t)(k_t F_t / Gamma_I) in fp32
                     if (sc == tr) sDg[tr] = accM[i];
-                }
-            }
-            // Kr = KF H for the block's 16 tokens, written channel-major (Kr^T) so that
-            // the record's Kr^T fragments are single 16-byte reads. This wave is
-            // otherwise idle until the off-diagonal blocks are done. A lane takes a
-            // token pair (16I + 2(lane & 7), +1) and eight-channel groups lane >> 3 and
-            // (lane >> 3) + 8, and writes each (channel, token pair) as one dword.
-            {
-                const int t0 = 16 * I + 2 * (lane & 7);
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    const int c0 = 8 * ((lane >> 3) + 8 * gg);
-                    // H (block I end -> chunk end) = product of the later block decays
-                    f32x4 h0 = {1.f, 1.f, 1.f, 1.f}, h1 = h0;
-#pragma unroll
-                    for (int K = 1; K < 4; ++K)
-                        if (K > I) {                                      // uniform
-                            h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
-                            h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
-                        }
-                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0);
-                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0 + 4);
-                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0);
-                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0 + 4);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float hh = e < 4 ? h0[e] : h1[e - 4];
-                        const float xa = (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
-                        const float xb = (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
-                        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-                        const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
-                        *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
-                    }
                 }
             }
         } else {
@@ -535,6 +504,40 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             else if (wave == 5) offdiag(IC<3>{}, IC<2>{}, IC<1>{});
             else if (wave == 6) offdiag(IC<2>{}, IC<0>{}, IC<2>{});
             else offdiag(IC<1>{}, IC<0>{}, IC<1>{});
+            // Kr = KF H for the 16 tokens of block I = wave - 4, written channel-major
+            // (Kr^T) so that the record's Kr^T fragments are single 16-byte reads. A
+            // lane takes a token pair (16I + 2(lane & 7), +1) and eight-channel groups
+            // lane >> 3 and (lane >> 3) + 8, and writes each (channel, token pair) as
+            // one dword.
+            {
+                const int I = wave & 3;
+                const int t0 = 16 * I + 2 * (lane & 7);
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int c0 = 8 * ((lane >> 3) + 8 * gg);
+                    // H (block I end -> chunk end) = product of the later block decays
+                    f32x4 h0 = {1.f, 1.f, 1.f, 1.f}, h1 = h0;
+#pragma unroll
+                    for (int K = 1; K < 4; ++K)
+                        if (K > I) {                                      // uniform
+                            h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
+                            h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
+                        }
+                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0);
+                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0 + 4);
+                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0);
+                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float hh = e < 4 ? h0[e] : h1[e - 4];
+                        const float xa = (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
+                        const float xb = (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
+                        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+                        const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
+                        *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
+                    }
+                }
+            }
         }
         // exact path for diagonal blocks whose in-block decay leaves the fp32 normal range
         for (int I = 0; I < 4 && (flags.x | flags.y | flags.z | flags.w); ++I) {
@@ -578,36 +581,39 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     if ((e & 15) >= (e >> 4)) sMqk[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<_Float16>(0.f);
             }
         }
+        // INV_II = (I + L_II)^{-1} of the diagonal blocks, as soon as L_II is final:
+        // wave = block, lane < 16 = column of INV_II, by column-oriented
+        // substitution: once x[sc] is final it is eliminated from every later row at
+        // once, so the updates of a step are independent and the L column reads
+        // (wave-uniform addresses, written by this wave) do not wait on the
+        // arithmetic. INV_II is stored transposed in the block's upper triangle;
+        // entries above the diagonal stay 0 (they only ever see x[sc] = 0).
+        if (wave < 4 && lane < 16) {
+            const int I = wave, col = lane;
+            float x[16];
+#pragma unroll
+            for (int tr = 0; tr < 16; ++tr) x[tr] = (tr == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int sc = 0; sc < 15; ++sc)
+#pragma unroll
+                for (int tr = sc + 1; tr < 16; ++tr) x[tr] -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
+#pragma unroll
+            for (int tr = 0; tr < 16; ++tr)
+                if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
+        }
         __syncthreads();
         fetch(next, 1);
         // the flags were read above (into registers); clear them for the next item
         if (tid < 4) sFlag[tid] = 0;
 
-        // ================= INV = (I + L)^{-1}, stored transposed in the upper triangle
-        // diagonal 16x16 blocks: wave = block, lane < 16 = column of INV_II, by
-        // column-oriented substitution: once x[sc] is final it is eliminated from
-        // every later row at once, so the updates of a step are independent and the
-        // L column reads (wave-uniform addresses) do not wait on the arithmetic.
-        // Entries above the diagonal stay 0 (they only ever see x[sc] = 0).
-        // Waves 0-3 also take their Kr^T record fragments, and waves 4-7 (token
-        // tile tt = wave - 4) build Kd^T for the W product (into LDS, over the F
-        // tile, which is dead now). Every record fragment is held in registers
-        // until the record is stored.
+        // ================= INV = (I + L)^{-1} off the diagonal blocks, and record fragments
+        // Waves 0-3 take their Kr^T record fragments and form the off-diagonal
+        // blocks of INV; waves 4-7 (token tile tt = wave - 4) build Kd^T for the W
+        // product (into LDS, over the F tile, which is dead now) and their Qd and
+        // Mqk record fragments. Every record fragment is held in registers until
+        // the record is stored.
         f16x8 fr[8];
         if (wave < 4) {
-            if (lane < 16) {
-                const int I = wave, col = lane;
-                float x[16];
-#pragma unroll
-                for (int tr = 0; tr < 16; ++tr) x[tr] = (tr == col) ? 1.f : 0.f;
-#pragma unroll
-                for (int sc = 0; sc < 15; ++sc)
-#pragma unroll
-                    for (int tr = sc + 1; tr < 16; ++tr) x[tr] -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
-#pragma unroll
-                for (int tr = 0; tr < 16; ++tr)
-                    if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
-            }
             // Kr^T record fragments: rows = channels 32w + 16rt + l16, k = tokens of
             // U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); Kr^T is final
             typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
@@ -650,8 +656,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                 }
             }
         }
-        __syncthreads();
-        fetch(next, 2);
         // off-diagonal blocks of INV on fp32 MFMA (exact products). With the 64 x 64
         // inverse taken as 2 x 2 blocks of 32 (A, D its diagonal halves, C its
         // lower-left block), INV = [[A^-1, 0], [-D^-1 C A^-1, D^-1]]:
@@ -730,8 +734,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sLI[(32 + 4 * lq + i) * SL + 48 + l16] = inv32t[i];  // INV_32
         } else {
-            // waves 4-7 (token tile tt), idle here, build their Qd and Mqk record
-            // fragments
             const int tt = wave & 3;
             // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
             // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
@@ -768,6 +770,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             }
         }
         __syncthreads();
+        fetch(next, 2);
 
         // ================= record: fp16 fragments of the scan's operands
         // Wavefront p: token tile tt = p & 3. Waves 0-3 (scan wavefront w = p)
