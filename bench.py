@@ -35,7 +35,9 @@ DECODE_WORKLOAD = "decode_512x32"
 # arithmetic of the timed prefill path (bf16 is only the I/O type)
 PREFILL_DTYPE = ("fp16 MFMA (state and U split into fp16 hi+lo) + fp32 MFMA, fp32 accumulate and state; "
                  "bf16 q/k/v/o")
-EXTRA_PREFILL_WORKLOADS = ("varlen_16x", "long_1m")
+EXTRA_PREFILL_WORKLOADS = ("varlen_16x", "long_1m", "long_1m_slow")
+# stress companions reported beside the graded workloads, labelled as such
+UNGRADED_WORKLOADS = {"long_1m_slow": "ungraded stress run: long_1m's shape with slow decay"}
 
 
 # Every leg's untimed warmup lasts at least this long (and at least `warmup`
@@ -131,7 +133,11 @@ def prefill_leg(pf, workload):
     tflops = pf["flops"] / k_s / 1e12
     gbps = pf["min_bytes"] / k_s / 1e9
     peak_tf, peak_bw = costs.MI355X_PEAK["bf16_TFLOPs"], costs.MI355X_PEAK["hbm_GBps"]
-    return {"sequences": pf["seqs"], "tokens": pf["tokens"], "H": w["H"],
+    leg = {"sequences": pf["seqs"], "tokens": pf["tokens"], "H": w["H"],
+           "gate": f"-softplus(N(0,1){w['shift']:+g})"}
+    if workload in UNGRADED_WORKLOADS:
+        leg["note"] = UNGRADED_WORKLOADS[workload]
+    return {**leg,
             "ms_per_call": round(pf["kernel_ms"], 4),
             "mtok_per_s": round(pf["tokens"] / k_s / 1e6, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf, "unit": "TFLOP/s",
@@ -259,7 +265,7 @@ def main():
     if not args.no_extra_workloads and args.workload == PREFILL_WORKLOAD:
         for wl in EXTRA_PREFILL_WORKLOADS:
             # the 1M-token workload's call takes ~30 ms: fewer calls
-            st = max(2, args.steps // 4) if wl == "long_1m" else args.steps
+            st = max(2, args.steps // 4) if wl.startswith("long_1m") else args.steps
             r = bench_prefill(st, min(args.warmup, 2), wl)
             del r["inputs"]
             torch.cuda.empty_cache()

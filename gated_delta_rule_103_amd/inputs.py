@@ -37,6 +37,10 @@ WORKLOADS: Dict[str, dict] = {
                           shift=2.0, state_std=0.02, seed=1003),
     "long_1m": dict(kind="prefill", B=1, H=16, T=1048576, D=128, C=64, io="bf16",
                     shift=4.0, s0_std=None, seed=1004),
+    # ungraded stress companion of long_1m: the same shape with slow decay,
+    # g = -softplus(N(0,1) - 4) (alpha ~ 0.97), so the state carries far
+    "long_1m_slow": dict(kind="prefill", B=1, H=16, T=1048576, D=128, C=64, io="bf16",
+                         shift=-4.0, s0_std=None, seed=1005),
 }
 WORKLOAD_ORDER: List[str] = ["tiny_f32", "single_seq_8k", "varlen_16x", "decode_512x32", "long_1m"]
 

@@ -5,7 +5,7 @@ preparation of the next window on a second stream beside the scan of the
 current one, the state passing from window to window through the workspace.
 Every token and head is compared with the fp64 oracle (same tolerances as the
 other bf16 tests), with a ragged last window, initial states, optional
-outputs, snapshots whose positions straddle window borders, the packed and
+outputs, slow decay, snapshots whose positions straddle window borders, the packed and
 per-head-gate kernel variants, run-to-run determinism, and a HIP-graph
 capture (where the pipeline stays on the captured stream) replayed several
 times with eager work between the replays.
@@ -99,6 +99,19 @@ def test_windowed_per_head_gate():
     o, S = gdn_prefill(d.q, d.k, d.v, g_head.cuda(), d.beta, None, C=C, out_dtype=torch.float32)
     torch.cuda.synchronize()
     ro, rS = oracle_prefill(replace(p, g=g_head[..., None].expand_as(p.g).contiguous()))
+    eo, eS = _errs(o, S, ro, rS)
+    assert eo <= TOL_BF16["o"] and eS <= TOL_BF16["S"]
+
+
+def test_windowed_slow_decay():
+    """Slow decay (alpha ~ 0.97): the state carries across every window border;
+    every token and head against the oracle."""
+    p = inputs.prefill(2, 128, B=1, T=T_LONG, C=C, io="bf16", gate="slow", s0_std=0.02, seed=308)
+    say(f"[windowed] slow decay: T={T_LONG} H=2")
+    d = to_dev(p)
+    o, S = kda_prefill(d.q, d.k, d.v, d.g, d.beta, d.S0, C=C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rS = oracle_prefill(p)
     eo, eS = _errs(o, S, ro, rS)
     assert eo <= TOL_BF16["o"] and eS <= TOL_BF16["S"]
 
