@@ -69,13 +69,6 @@ template <typename T>
 __device__ __forceinline__ T buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-template <typename T> __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, int voff, float x);
-template <> __device__ __forceinline__ void buf_st<float>(__amdgpu_buffer_rsrc_t r, int voff, float x) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, 0, 0);
-}
-template <> __device__ __forceinline__ void buf_st<bf16_t>(__amdgpu_buffer_rsrc_t r, int voff, float x) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)), r, voff, 0, 0);
-}
 
 // four consecutive outputs with one store (16 bytes fp32, 8 bytes bf16)
 template <typename T> __device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x);
@@ -95,11 +88,6 @@ template <typename T> __device__ __forceinline__ float ld_scalar(const T *p, siz
 template <> __device__ __forceinline__ float ld_scalar<float>(const float *p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld_scalar<bf16_t>(const bf16_t *p, size_t i) {
     return bf16_to_f32(p[i]);
-}
-template <typename T> __device__ __forceinline__ void st_scalar(T *p, size_t i, float x);
-template <> __device__ __forceinline__ void st_scalar<float>(float *p, size_t i, float x) { p[i] = x; }
-template <> __device__ __forceinline__ void st_scalar<bf16_t>(bf16_t *p, size_t i, float x) {
-    p[i] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x));
 }
 
 // x = hi + lo, hi = fp16(x), lo = fp16(x - hi): about 22 significant bits for
@@ -1279,7 +1267,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     constexpr int LPW = Rec::DG / 128 / (4 * TEAM);                 // lines per wavefront
     const int touch_off = ((member * 4 + w4) * LPW + lane % LPW) * 128;  // < Rec::DG
     uint32_t touch_acc = 0, touch_prev = 0;
-    auto ostep = [&](OFrags &f, int j, const OFrags &f1, OFrags &nf, int nj) {
+    auto ostep = [&](OFrags &f, int j, OFrags &nf, int nj) {
         const int bsel = j & 1;
         touch_acc ^= touch_prev;
         touch_prev = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(j + 3, last)), touch_off, 0, 0);
@@ -1343,17 +1331,17 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     __syncthreads();                                         // A: the initial state is in LDS
     // rounds of six steps, as for the recurrence
     for (int j = j0; j < j1; j += 6) {
-        ostep(A, j, B, Cb, min(j + 2, last));
+        ostep(A, j, Cb, min(j + 2, last));
         if (j + 1 >= j1) break;
-        ostep(B, j + 1, Cb, A, min(j + 3, last));
+        ostep(B, j + 1, A, min(j + 3, last));
         if (j + 2 >= j1) break;
-        ostep(Cb, j + 2, A, B, min(j + 4, last));
+        ostep(Cb, j + 2, B, min(j + 4, last));
         if (j + 3 >= j1) break;
-        ostep(A, j + 3, B, Cb, min(j + 5, last));
+        ostep(A, j + 3, Cb, min(j + 5, last));
         if (j + 4 >= j1) break;
-        ostep(B, j + 4, Cb, A, min(j + 6, last));
+        ostep(B, j + 4, A, min(j + 6, last));
         if (j + 5 >= j1) break;
-        ostep(Cb, j + 5, A, B, min(j + 7, last));
+        ostep(Cb, j + 5, B, min(j + 7, last));
     }
     asm volatile("" ::"v"(touch_acc ^ touch_prev));
 }
