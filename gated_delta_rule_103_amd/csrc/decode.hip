@@ -1,124 +1,93 @@
 // decode.hip -- single-token KDA decode, state updated in place.
 //
 // One step of the recurrence in the Kimi K3 explainer's FlashKDA paragraph
-// (decode follows the D_t / u_t form): M' = Diag(exp g) M, u = beta (v - M'^T k),
-// M = M' + k u^T, o = M^T q. The explainer's cost model for it is about 7*D^2
-// FLOPs and 8*D^2 bytes per head: the fp32 state is read once and written
-// once, so the kernel is a stream over HBM.
+// (decode follows the D_t / u_t form), on the state S [Dv][Dk] (row c = value
+// channel, column = key channel):
+//     S' = S Diag(exp g),  u = beta (v - S' k),  S = S' + u k^T,  o = S q.
+// The explainer's cost model for it is about 7*D^2 FLOPs and 8*D^2 bytes per
+// head: the fp32 state is read once and written once, so the kernel is a
+// stream over HBM.
 //
-// Layout of the work: the D value columns of one (sequence, head) chain are
-// split over two workgroups (the reductions run over key rows, so column
-// slices are independent). A thread owns one float4 column group of every
-// (NT*4/W)-th row of its slice; each wavefront reads whole 256-byte row
-// slices, and the state stays in registers between the read and the write.
-// o is formed from the same pass: o = M'^T q + (q.k) u, so only one reduction
-// round is needed. The state is read with ordinary loads and written with
-// streaming (non-temporal) stores, which measured fastest.
+// Layout of the work: every quantity of a row reduces over that row's key
+// channels, and a row is D*4 contiguous bytes. D/4 consecutive lanes own a
+// row (four key channels, one float4, each), so both reductions (S'k and S'q)
+// are sums over those lanes by cross-lane shuffles: no LDS, no barrier. A
+// thread holds four rows, a workgroup 4 x (threads / (D/4)) rows, and each
+// wavefront instruction reads or writes whole adjacent rows (1 KB at D = 128).
+// o = S'q + (q.k) u is formed from the same pass. The state is read and
+// written with the non-temporal hint (each byte is touched once).
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-template <int D, int NT, int W, typename TI, typename TB, typename TO>
+// sum over each group of W consecutive lanes (W a power of two, at most 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) x += __shfl_xor(x, o, W);
+    return x;
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
+template <int D, int NT, typename TI, typename TB, typename TO>
 __global__ __launch_bounds__(NT) void decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                     const TI *__restrict__ v, const float *__restrict__ g,
                                                     const TB *__restrict__ beta, float *__restrict__ S,
                                                     TO *__restrict__ out, bool g_head, bool qk_norm, float norm_eps) {
-    // NT threads cover W columns of one chain: the reductions over key rows stay
-    // inside the workgroup, so the columns of a chain are split over D / W
-    // workgroups.
-    constexpr int CG = W / 4;         // float4 column groups per workgroup
-    constexpr int RG = NT / CG;       // row groups (threads sharing a column group)
-    constexpr int RPT = D / RG;       // rows per thread
-    static_assert(CG * RG == NT && RG * RPT == D, "decode tiling");
-    __shared__ float s_q[D], s_k[D], s_a[D], s_u[W];
-    __shared__ float s_red[2][RG][W];
-    __shared__ float s_qk, s_nq, s_nk;
-
-    constexpr int SPLIT = D / W;
+    constexpr int LPR = D / 4;            // lanes per state row
+    constexpr int SLOTS = NT / LPR;       // rows a workgroup takes per pass
+    constexpr int ROWS = 4 * SLOTS;       // rows per workgroup
+    constexpr int SPLIT = D / ROWS;       // workgroups per chain
+    static_assert(NT % LPR == 0 && D % ROWS == 0 && (LPR & (LPR - 1)) == 0 && 64 % LPR == 0, "decode tiling");
     const size_t chain = blockIdx.x / SPLIT;
-    const int col0 = (blockIdx.x % SPLIT) * W;
-    const int t = threadIdx.x;
-    const int cg = t % CG, rg = t / CG;
-    f32x4 *Sp = reinterpret_cast<f32x4 *>(S + chain * D * D + col0);
+    const int r0 = (blockIdx.x % SPLIT) * ROWS, t = threadIdx.x, kq = t % LPR, slot = t / LPR;
+    f32x4 *Sp = reinterpret_cast<f32x4 *>(S + chain * D * D);
 
-    f32x4 m[RPT];
+    f32x4 s[4];
+    float vr[4];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) m[i] = Sp[(rg + RG * i) * (D / 4) + cg];
-
-    for (int c = t; c < D; c += NT) {
-        s_q[c] = io<TI>::load(q, chain * D + c);
-        s_k[c] = io<TI>::load(k, chain * D + c);
-        s_a[c] = expf(GateRow(g, g_head, chain, D).at(c));
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + slot + SLOTS * i;
+        s[i] = __builtin_nontemporal_load(&Sp[row * (D / 4) + kq]);
+        vr[i] = io<TI>::load(v, chain * D + row);
     }
-    __syncthreads();
-    if (t < 64) {
-        float x = 0.f, xq = 0.f, xk = 0.f;
-        for (int c = t; c < D; c += 64) {
-            x += s_q[c] * s_k[c];
-            xq += s_q[c] * s_q[c];
-            xk += s_k[c] * s_k[c];
-        }
-        x = warp_sum(x);
-        xq = warp_sum(xq);
-        xk = warp_sum(xk);
-        if (t == 0) {
-            // L2-normalised q and k: x / sqrt(sum x^2 + eps), applied as two scalars
-            const float nq = qk_norm ? 1.f / sqrtf(xq + norm_eps) : 1.f;
-            const float nk = qk_norm ? 1.f / sqrtf(xk + norm_eps) : 1.f;
-            s_qk = x * nq * nk;
-            s_nq = nq;
-            s_nk = nk;
-        }
-    }
-    float nq = 1.f, nk = 1.f;
-    if (qk_norm) {                                     // uniform
-        __syncthreads();
-        nq = s_nq;
-        nk = s_nk;
-    }
-
-    float4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+    const float b = io<TB>::load(beta, chain);
+    // this lane's key channels 4kq .. 4kq + 3
+    const GateRow gate(g, g_head, chain, D);
+    f32x4 q4, k4, a4;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + RG * i;
-        const float a = s_a[r], kr = s_k[r] * nk, qr = s_q[r] * nq;
-        m[i].x *= a; m[i].y *= a; m[i].z *= a; m[i].w *= a;
-        pk.x += kr * m[i].x; pk.y += kr * m[i].y; pk.z += kr * m[i].z; pk.w += kr * m[i].w;
-        pq.x += qr * m[i].x; pq.y += qr * m[i].y; pq.z += qr * m[i].z; pq.w += qr * m[i].w;
+    for (int e = 0; e < 4; ++e) {
+        q4[e] = io<TI>::load(q, chain * D + 4 * kq + e);
+        k4[e] = io<TI>::load(k, chain * D + 4 * kq + e);
+        a4[e] = expf(gate.at(4 * kq + e));
     }
-    *reinterpret_cast<float4 *>(&s_red[0][rg][4 * cg]) = pk;
-    *reinterpret_cast<float4 *>(&s_red[1][rg][4 * cg]) = pq;
-    __syncthreads();
-    if (t < W) {
-        float p = 0.f, r = 0.f;
-#pragma unroll
-        for (int j = 0; j < RG; ++j) { p += s_red[0][j][t]; r += s_red[1][j][t]; }
-        const float b = io<TB>::load(beta, chain);
-        const float u = b * (io<TI>::load(v, chain * D + col0 + t) - p);
-        s_u[t] = u;
-        io<TO>::store(out, chain * D + col0 + t, r + s_qk * u);
+    if (qk_norm) {                                       // uniform
+        // L2-normalised q and k: x / sqrt(sum x^2 + eps)
+        q4 *= 1.f / sqrtf(group_sum<LPR>(dot4(q4, q4)) + norm_eps);
+        k4 *= 1.f / sqrtf(group_sum<LPR>(dot4(k4, k4)) + norm_eps);
     }
-    __syncthreads();
-    const float4 u4 = *reinterpret_cast<const float4 *>(&s_u[4 * cg]);
+    const float qk = group_sum<LPR>(dot4(q4, k4));
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + RG * i;
-        const float kr = s_k[r] * nk;
-        f32x4 x = m[i];
-        x.x += kr * u4.x; x.y += kr * u4.y; x.z += kr * u4.z; x.w += kr * u4.w;
-        __builtin_nontemporal_store(x, &Sp[r * (D / 4) + cg]);
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + slot + SLOTS * i;
+        const f32x4 x = s[i] * a4;                       // S' = S Diag(exp g)
+        const float pk = group_sum<LPR>(dot4(x, k4));    // (S' k)_row
+        const float pq = group_sum<LPR>(dot4(x, q4));    // (S' q)_row
+        const float u = b * (vr[i] - pk);
+        __builtin_nontemporal_store(x + k4 * u, &Sp[row * (D / 4) + kq]);
+        if (kq == 0) io<TO>::store(out, chain * D + row, pq + qk * u);
     }
 }
 
-// 128 threads per workgroup, each workgroup one half (64 value columns) of a
-// chain's state: two workgroups per (sequence, head)
+// D = 128: 512 threads, two workgroups of 64 rows per (sequence, head);
+// D = 64: 256 threads, one workgroup of 64 rows
 template <int D, typename TI, typename TB, typename TO>
 hipError_t launch_t(const DecodeArgs &a) {
-    constexpr int NT = 128, W = D / 2;
+    constexpr int NT = D == 128 ? 512 : 256, SPLIT = D / (4 * NT / (D / 4));
     const unsigned chains = static_cast<unsigned>(a.N) * static_cast<unsigned>(a.H);
-    hipLaunchKernelGGL((decode_kernel<D, NT, W, TI, TB, TO>), dim3(chains * (D / W)), dim3(NT), 0, a.stream,
+    hipLaunchKernelGGL((decode_kernel<D, NT, TI, TB, TO>), dim3(chains * SPLIT), dim3(NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
                        a.g, static_cast<const TB *>(a.beta), a.S, static_cast<TO *>(a.out), a.g_head, a.qk_norm,
                        a.norm_eps);

@@ -38,7 +38,7 @@ struct SeqView {
 // base[((n * H + h) * max + k - 1) * Dk * Dv + ...]. Only boundaries inside the
 // sequence (k * every * C <= length) are written.
 struct SnapView {
-    float *base;    // [N][H][max][Dk][Dv] fp32, or nullptr
+    float *base;    // [N][H][max][Dv][Dk] fp32, or nullptr
     int every;      // chunks between snapshots (> 0 when base is set)
     int max;        // snapshots per sequence
     __device__ float *slot(int n, int h, int H, int chunks_done, int len, int C, int DD) const {

@@ -23,7 +23,7 @@ struct PrefillArgs {
     void *ws;
     size_t ws_bytes;
     hipStream_t stream;
-    // optional state snapshots: [N][H][max_snaps][Dk][Dv] fp32, one every
+    // optional state snapshots: [N][H][max_snaps][Dv][Dk] fp32, one every
     // snap_every chunks of each sequence (nullptr: none)
     float *snaps = nullptr;
     int snap_every = 0, max_snaps = 0;

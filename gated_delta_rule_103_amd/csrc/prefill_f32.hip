@@ -168,9 +168,10 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ rec
     const int n = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * TV, t = threadIdx.x;
     const size_t st = ((size_t)n * H + h) * D * D;
 
+    // the state S [Dv][Dk] in memory: row j0 + j, key channel c
     for (int p = t; p < D * TV; p += 256) {
-        const int c = p / TV, j = p % TV;
-        s_M[c][j] = S0 ? S0[st + (size_t)c * D + j0 + j] : 0.f;
+        const int j = p / D, c = p % D;
+        s_M[c][j] = S0 ? S0[st + (size_t)(j0 + j) * D + c] : 0.f;
     }
     __syncthreads();
 
@@ -208,15 +209,15 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ rec
         __syncthreads();
         if (float *sp = snap.slot(n, h, H, j + 1, len, C, D * D)) {     // uniform across the workgroup
             for (int p = t; p < D * TV; p += 256) {
-                const int c = p / TV, jj = p % TV;
-                sp[(size_t)c * D + j0 + jj] = s_M[c][jj];
+                const int jj = p / D, c = p % D;
+                sp[(size_t)(j0 + jj) * D + c] = s_M[c][jj];
             }
         }
     }
     if (S_out) {
         for (int p = t; p < D * TV; p += 256) {
-            const int c = p / TV, j = p % TV;
-            S_out[st + (size_t)c * D + j0 + j] = s_M[c][j];
+            const int j = p / D, c = p % D;
+            S_out[st + (size_t)(j0 + j) * D + c] = s_M[c][j];
         }
     }
 }

@@ -8,7 +8,8 @@
 //     Mqk[t,s] = sum_c q_t k_s exp(a_t - a_s)   (s <= t)
 //     L[t,s]   = beta_t sum_c k_t k_s exp(a_t - a_s)   (s < t)
 //     IB       = (I + L)^{-1} Diag(beta),   W = IB Kd,   U~ = IB V
-// and per chunk of one (sequence, head), with the state M = S^T:
+// and per chunk of one (sequence, head), with M = S^T (S [Dv][Dk] is the state
+// as it is stored; the kernels work on its transpose):
 //     U     = U~ - W M
 //     O     = Qd M + Mqk U
 //     M_out = Diag(gamma) M + Kr^T U
@@ -988,30 +989,28 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
 
     if (wave < 4) {
         // ============================ recurrence
+        // the state S [Dv][Dk] in memory: this lane's four channels 32w + 16rt + 4lq
+        // .. +3 of value column col are one 16-byte piece of row col
+        auto st_at = [&](int rt, int nt) {
+            return st_off + (size_t)(col0 + 16 * nt + l16) * D + 32 * w4 + 16 * rt + 4 * lq;
+        };
         f32x4 Macc[2][NT];
         float m0 = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt) {
+                Macc[rt][nt] = S_in ? *reinterpret_cast<const f32x4 *>(S_in + st_at(rt, nt)) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                    Macc[rt][nt][i] = S_in ? S_in[st_off + (size_t)chn * D + col] : 0.f;
-                    m0 = fmaxf(m0, fabsf(Macc[rt][nt][i]));
-                }
+                for (int i = 0; i < 4; ++i) m0 = fmaxf(m0, fabsf(Macc[rt][nt][i]));
+            }
         if (j0 >= j1) {
             // nothing to scan in this launch; an empty sequence: S_out = S0 exactly
             if (nch == 0 && p.S_out)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                            p.S_out[st_off + (size_t)chn * D + col] = Macc[rt][nt][i];
-                        }
+                    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4 *>(p.S_out + st_at(rt, nt)) = Macc[rt][nt];
             return;
         }
         m0 = wave_max(m0);
@@ -1139,11 +1138,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                            sp[(size_t)chn * D + col] = Macc[rt][nt][i] * inv;
-                        }
+                        *reinterpret_cast<f32x4 *>(sp + (st_at(rt, nt) - st_off)) = Macc[rt][nt] * inv;
             }
             publish();
             issue(rn, nf, 10);
@@ -1189,12 +1184,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int chn = 32 * w4 + 16 * rt + 4 * lq + i, col = col0 + 16 * nt + l16;
-                        S_fin[st_off + (size_t)chn * D + col] = Macc[rt][nt][i] * inv;
-                    }
+                for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4 *>(S_fin + st_at(rt, nt)) = Macc[rt][nt] * inv;
         }
         return;
     }

@@ -64,7 +64,7 @@ class PrefillInputs:
     v: torch.Tensor            # [B, T, H, Dv] io dtype
     g: torch.Tensor            # [B, T, H, Dk] fp32
     beta: torch.Tensor         # [B, T, H]     beta dtype
-    S0: Optional[torch.Tensor]  # [N, H, Dk, Dv] fp32 or None
+    S0: Optional[torch.Tensor]  # [N, H, Dv, Dk] fp32 (the state S, row = value channel) or None
     cu_seqlens: Optional[torch.Tensor]  # int32 [N+1] (B == 1) or None
     C: int
     meta: dict = field(default_factory=dict)
@@ -121,7 +121,7 @@ def prefill(H: int, D: int, *, B: int = 1, T: Optional[int] = None,
         raise ValueError(gate)
     beta = torch.sigmoid(rn(B, T, H)).to(bdt)
     N = B if cu is None else cu.numel() - 1
-    S0 = None if s0_std is None else (rn(N, H, Dk, Dv) * s0_std)
+    S0 = None if s0_std is None else (rn(N, H, Dv, Dk) * s0_std)
     if v_zero:
         v = torch.zeros_like(v)
     if beta_one:
@@ -161,7 +161,7 @@ class DecodeInputs:
     v: torch.Tensor     # [steps, N, H, Dv]
     g: torch.Tensor     # [steps, N, H, Dk] fp32
     beta: torch.Tensor  # [steps, N, H]
-    state: torch.Tensor  # [N, H, Dk, Dv] fp32 (initial; the kernel updates a copy in place)
+    state: torch.Tensor  # [N, H, Dv, Dk] fp32 (initial; the kernel updates a copy in place)
 
 
 def decode(N: int, H: int, D: int, steps: int, *, io: str = "bf16", shift: float = 2.0,

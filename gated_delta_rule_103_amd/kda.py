@@ -173,11 +173,11 @@ def _check_prefill(q, k, v, g, beta, S0, out, S_out, cu_seqlens, workspace, g_he
         N = cu_seqlens.numel() - 1
     else:
         N = B
-    _expect(S0, "S0", (N, H, Dk, Dv), (torch.float32,), optional=True)
+    _expect(S0, "S0", (N, H, Dv, Dk), (torch.float32,), optional=True)
     _expect(out, "out", (B, T, H, Dv), _FLOAT_IO, optional=True)
-    _expect(S_out, "S_out", (N, H, Dk, Dv), (torch.float32,), optional=True)
+    _expect(S_out, "S_out", (N, H, Dv, Dk), (torch.float32,), optional=True)
     if snapshots is not None:
-        _expect(snapshots, "snapshots", (N, H, max_snapshots, Dk, Dv), (torch.float32,))
+        _expect(snapshots, "snapshots", (N, H, max_snapshots, Dv, Dk), (torch.float32,))
     if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.dim() != 1 or
                                   workspace.dtype != torch.uint8):
         raise ValueError("workspace must be a 1-D uint8 tensor")
@@ -192,7 +192,7 @@ def _prefill_buffers(lib, q, v, beta, cu_seqlens, C, out, S_out, out_dtype, work
     if out is None:
         out = torch.empty(B, T, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
     if S_out is None and return_state:
-        S_out = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
+        S_out = torch.empty(N, H, Dv, Dk, dtype=torch.float32, device=q.device)
     need = int(lib.kda_prefill_workspace_size(N, B * T, H, Dk, Dv, C, _dt(q)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -225,9 +225,9 @@ def kda_prefill(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_seqlens=N
                 out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
                 return_state: bool = True, qk_l2norm: bool = False, l2norm_eps: float = 1e-6):
     """Chunked KDA prefill. q, k, g: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
-    S0: [N, H, Dk, Dv] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B == 1) or None.
+    S0: [N, H, Dv, Dk] fp32 (the state S, row = value channel) or None; cu_seqlens: int32 [N+1] device tensor (B == 1) or None.
     qk_l2norm: L2-normalise q and k over Dk inside the kernels (x / sqrt(sum x^2 + eps)).
-    Returns (out [B, T, H, Dv], S_out [N, H, Dk, Dv] or None)."""
+    Returns (out [B, T, H, Dv], S_out [N, H, Dv, Dk] or None)."""
     return _prefill("kda_prefill", q, k, v, g, beta, S0, out, S_out, cu_seqlens, C, out_dtype, workspace,
                     stream, return_state, qk_l2norm, l2norm_eps)
 
@@ -246,7 +246,7 @@ def kda_prefill_noalloc(q, k, v, g, beta, S0=None, *, out=None, S_out=None, cu_s
     if out is None:
         out = torch.empty(B, T, H, Dv, dtype=out_dtype or q.dtype, device=q.device)
     if S_out is None and return_state:
-        S_out = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=q.device)
+        S_out = torch.empty(N, H, Dv, Dk, dtype=torch.float32, device=q.device)
     with torch.cuda.device(dev):
         st = lib.kda_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(out),
                                      _ptr(S_out), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, C, _dt(q), _dt(beta),
@@ -271,14 +271,14 @@ def kda_prefill_snapshots(q, k, v, g, beta, S0=None, *, snapshot_every: int, max
                           out_dtype: Optional[torch.dtype] = None, workspace=None, stream=None,
                           return_state: bool = True):
     """kda_prefill that also writes the state after every ``snapshot_every`` tokens of
-    each sequence into ``snapshots`` [N, H, max_snapshots, Dk, Dv] fp32 (slots past a
+    each sequence into ``snapshots`` [N, H, max_snapshots, Dv, Dk] fp32 (slots past a
     sequence's end are not written). Returns (out, S_out, snapshots)."""
     lib = load_library()
     if snapshots is None:
         if not isinstance(q, torch.Tensor) or q.dim() != 4 or not isinstance(v, torch.Tensor) or v.dim() != 4:
             raise ValueError("q must be [B, T, H, Dk] and v [B, T, H, Dv]")
         N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
-        snapshots = torch.full((N, q.shape[2], max_snapshots, q.shape[3], v.shape[3]), float("nan"),
+        snapshots = torch.full((N, q.shape[2], max_snapshots, v.shape[3], q.shape[3]), float("nan"),
                                dtype=torch.float32, device=q.device)
     dev = _check_prefill(q, k, v, g, beta, S0, out, S_out, cu_seqlens, workspace, False, snapshots,
                          max_snapshots)
@@ -308,7 +308,7 @@ def _decode(entry, q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm=False,
     else:
         _expect(g, "g", (N, H, Dk), (torch.float32,))
     _expect(beta, "beta", (N, H), _FLOAT_IO)
-    _expect(S, "S", (N, H, Dk, Dv), (torch.float32,))
+    _expect(S, "S", (N, H, Dv, Dk), (torch.float32,))
     _expect(out, "out", (N, H, Dv), _FLOAT_IO, optional=True)
     dev = _same_gpu(q=q, k=k, v=v, g=g, beta=beta, S=S, out=out)
     if out is None:
@@ -330,7 +330,7 @@ def _decode(entry, q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm=False,
 
 def kda_decode(q, k, v, g, beta, S, *, out=None, out_dtype: Optional[torch.dtype] = None,
                stream=None, qk_l2norm: bool = False, l2norm_eps: float = 1e-6):
-    """One decode step, state S [N, H, Dk, Dv] fp32 updated in place.
+    """One decode step, state S [N, H, Dv, Dk] fp32 (row = value channel) updated in place.
     q, k, g: [N, H, Dk]; v: [N, H, Dv]; beta: [N, H]. Returns out [N, H, Dv]."""
     return _decode("kda_decode", q, k, v, g, beta, S, out, out_dtype, stream, qk_l2norm, l2norm_eps)
 

@@ -12,12 +12,13 @@
  *   pseudo-values U), the cumulative decay a being one value per token.
  *
  * Per (sequence, head) chain and token t, with alpha_t = exp(g_t):
- *     M'  = Diag(alpha_t) M_{t-1}
- *     u_t = beta_t (v_t - M'^T k_t)
- *     M_t = M' + k_t u_t^T
- *     o_t = M_t^T q_t
- * The state is stored as M = S^T: shape [Dk][Dv], row = key channel, Dv
- * contiguous, fp32. No 1/sqrt(D) scale and no normalisation is applied;
+ *     S'  = S_{t-1} Diag(alpha_t)
+ *     u_t = beta_t (v_t - S' k_t)
+ *     S_t = S' + u_t k_t^T
+ *     o_t = S_t q_t
+ * The state S is stored as written here: shape [Dv][Dk], row = value
+ * channel, Dk contiguous, fp32 (so a row's reductions over the key channels
+ * read contiguous memory). No 1/sqrt(D) scale and no normalisation is applied;
  * q and k arrive already normalised if the model wants them so.
  *
  * Conventions for every call
@@ -116,9 +117,9 @@ size_t kda_prefill_workspace_size(int N, int T_total, int H, int Dk, int Dv, int
  *   g      [T_total][H][Dk]   fp32, natural-log decay (alpha = exp(g); g <= 0
  *                              is the intended domain, g = -inf wipes a channel)
  *   beta   [T_total][H]       beta_dtype
- *   S0     [N][H][Dk][Dv]     fp32 initial state, or NULL for a zero state
+ *   S0     [N][H][Dv][Dk]     fp32 initial state, or NULL for a zero state
  *   out    [T_total][H][Dv]   out_dtype, o_t for every token
- *   S_out  [N][H][Dk][Dv]     fp32 final state, or NULL to skip it; may be
+ *   S_out  [N][H][Dv][Dk]     fp32 final state, or NULL to skip it; may be
  *                              the same pointer as S0 (updated in place)
  *   cu_seqlens  int32 [N+1] device array of token offsets with
  *               cu_seqlens[0] = 0 and cu_seqlens[N] = T_total (varlen, then
@@ -207,7 +208,7 @@ int kda_prefill_noalloc(const void *q, const void *k, const void *v, const float
  *   snapshot_every  tokens between snapshots, a multiple of C (else
  *                   KDA_ERR_UNSUPPORTED), >= 1
  *   max_snapshots   capacity per sequence, >= 1
- *   snapshots       [N][H][max_snapshots][Dk][Dv] fp32 device buffer (not NULL).
+ *   snapshots       [N][H][max_snapshots][Dv][Dk] fp32 device buffer (not NULL).
  *                   Slot k-1 of sequence n receives the state after its first
  *                   k * snapshot_every tokens, for every k >= 1 with
  *                   k * snapshot_every <= length(n) and k <= max_snapshots.
@@ -250,8 +251,8 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g,
  *
  *   q, k   [N][H][Dk]  io_dtype        v    [N][H][Dv]  io_dtype
  *   g      [N][H][Dk]  fp32            beta [N][H]      beta_dtype
- *   S      [N][H][Dk][Dv] fp32, read and overwritten with the new state
- *   out    [N][H][Dv]  out_dtype, o_t = M_t^T q_t
+ *   S      [N][H][Dv][Dk] fp32, read and overwritten with the new state
+ *   out    [N][H][Dv]  out_dtype, o_t = S_t q_t
  * Support: Dk == Dv in {64, 128}; io_dtype KDA_BF16 or KDA_F32; beta_dtype
  * and out_dtype either; N*H >= 1.
  */

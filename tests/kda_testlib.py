@@ -32,9 +32,33 @@ def to_dev(p, device="cuda"):
                    cu_seqlens=mv(p.cu_seqlens))
 
 
+def orc_state(S):
+    """A state in the library's layout, S [..., Dv, Dk] (value channel x key
+    channel), as the oracle takes it, M = S^T [..., Dk, Dv]; the same swap maps
+    the oracle's states back. float64 numpy (a torch tensor is upcast); None
+    passes through."""
+    if S is None:
+        return None
+    S = host64(S) if hasattr(S, "detach") else np.asarray(S, dtype=np.float64)
+    return np.ascontiguousarray(np.swapaxes(S, -1, -2))
+
+
+def oracle_recurrent(q, k, v, g, beta, S0=None, **kw):
+    """oracle.recurrent with its states (S0 in, S_out out) in the library's layout."""
+    o, S = oracle.recurrent(q, k, v, g, beta, S0=orc_state(S0), **kw)
+    return o, orc_state(S)
+
+
+def oracle_decode_step(q, k, v, g, beta, S, **kw):
+    """oracle.decode_step with the state in the library's layout."""
+    o, S_new = oracle.decode_step(q, k, v, g, beta, orc_state(S), **kw)
+    return o, orc_state(S_new)
+
+
 def oracle_prefill(p, chains=None):
     """fp64 oracle on the exact (rounded) inputs of PrefillInputs p.
-    Returns (o [T_total, H, Dv], S [N, H, Dk, Dv]) as float64."""
+    Returns (o [T_total, H, Dv], S [N, H, Dv, Dk]) as float64, the state in
+    the library's layout."""
     H = p.q.shape[2]
     q, k, v, g = (host64(x).reshape(-1, H, x.shape[-1]) for x in (p.q, p.k, p.v, p.g))
     beta = host64(p.beta).reshape(-1, H)
@@ -43,8 +67,7 @@ def oracle_prefill(p, chains=None):
     else:
         B, T = p.q.shape[0], p.q.shape[1]
         cu = np.arange(B + 1, dtype=np.int64) * T
-    s0 = None if p.S0 is None else host64(p.S0)
-    return oracle.recurrent(q, k, v, g, beta, S0=s0, cu_seqlens=cu)
+    return oracle_recurrent(q, k, v, g, beta, S0=p.S0, cu_seqlens=cu)
 
 
 def gpu_prefill(p, out_dtype=None, S_out=True, C=None):

@@ -14,9 +14,8 @@ from dataclasses import replace
 import pytest
 import torch
 
-import oracle
 from gated_delta_rule_103_amd import gdn_decode, gdn_prefill, inputs
-from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_prefill, rel_err, to_dev
+from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_decode_step, oracle_prefill, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +86,7 @@ def test_gdn_decode(D, gated):
         o = gdn_decode(*args, None if gh is None else gh.cuda(), x.beta[s].cuda().contiguous(), S,
                        out_dtype=torch.float32)
         gref = torch.zeros_like(x.g[s]) if gh is None else gh[..., None].expand_as(x.g[s])
-        ro, Sref = oracle.decode_step(x.q[s], x.k[s], x.v[s], gref, x.beta[s], Sref)
+        ro, Sref = oracle_decode_step(x.q[s], x.k[s], x.v[s], gref, x.beta[s], Sref)
         torch.cuda.synchronize()
         assert rel_err(host64(o), ro) <= 1e-5
     assert rel_err(host64(S), Sref) <= 1e-5

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from gated_delta_rule_103_amd import gdn_decode, gdn_prefill, inputs, kda_decode, kda_prefill
-from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_prefill, rel_err, to_dev
+from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_decode_step, oracle_prefill, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
@@ -80,7 +80,7 @@ def test_decode_qk_l2norm(D, head_gate):
             o = kda_decode(q, k, v, x.g[s].cuda().contiguous(), b, S, out_dtype=torch.float32, qk_l2norm=True,
                            l2norm_eps=EPS)
             gref = x.g[s]
-        ro, Sref = oracle.decode_step(oracle.l2norm(host64(x.q[s]), EPS), oracle.l2norm(host64(x.k[s]), EPS),
+        ro, Sref = oracle_decode_step(oracle.l2norm(host64(x.q[s]), EPS), oracle.l2norm(host64(x.k[s]), EPS),
                                       x.v[s], gref, x.beta[s], Sref)
         torch.cuda.synchronize()
         assert rel_err(host64(o), ro) <= 1e-5

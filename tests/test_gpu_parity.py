@@ -15,9 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from gated_delta_rule_103_amd import inputs, kda_decode, kda_prefill
-from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_prefill, rel_err, to_dev
+from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_decode_step, oracle_prefill, oracle_recurrent, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +83,7 @@ def test_decode_small(D, io):
     for s in range(steps):
         args = [t[s].cuda().contiguous() for t in (x.q, x.k, x.v, x.g, x.beta)]
         o = kda_decode(*args, S, out_dtype=torch.float32)
-        ro, Sref = oracle.decode_step(*(t[s] for t in (x.q, x.k, x.v, x.g, x.beta)), Sref)
+        ro, Sref = oracle_decode_step(*(t[s] for t in (x.q, x.k, x.v, x.g, x.beta)), Sref)
         torch.cuda.synchronize()
         assert rel_err(host64(o), ro) <= 1e-5
     assert rel_err(host64(S), Sref) <= 1e-5
@@ -117,7 +116,7 @@ def test_decode_workload_512x32_64_steps():
     torch.cuda.synchronize()
     # token-major packed layout for the oracle: sequence n holds its 64 steps in order
     pack = lambda t: host64(t.transpose(0, 1).contiguous()).reshape(N * steps, H, -1)
-    ro, rS = oracle.recurrent(pack(x.q), pack(x.k), pack(x.v), pack(x.g),
+    ro, rS = oracle_recurrent(pack(x.q), pack(x.k), pack(x.v), pack(x.g),
                               host64(x.beta.transpose(0, 1).contiguous()).reshape(N * steps, H),
                               S0=host64(x.state), cu_seqlens=np.arange(N + 1, dtype=np.int64) * steps)
     ro = ro.reshape(N, steps, H, D).transpose(1, 0, 2, 3)       # [steps, N, H, D]
@@ -265,7 +264,7 @@ def test_prefill_long_1m_workload():
     for a in range(0, T, Wn):
         b = min(T, a + Wn)
         cut = lambda t: host64(t[0, a:b])
-        ro, state = oracle.recurrent(cut(p.q), cut(p.k), cut(p.v), cut(p.g), host64(p.beta[0, a:b]),
+        ro, state = oracle_recurrent(cut(p.q), cut(p.k), cut(p.v), cut(p.g), host64(p.beta[0, a:b]),
                                      S0=state)
         got = host64(o[0, a:b])
         err_max = max(err_max, float(np.abs(got - ro).max()))
@@ -296,7 +295,7 @@ def test_prefill_long_1m_slow_decay_stress():
     for a in range(0, T, Wn):
         b = min(T, a + Wn)
         cut = lambda t: host64(t[0, a:b, heads])
-        ro, state = oracle.recurrent(cut(p.q), cut(p.k), cut(p.v), cut(p.g), host64(p.beta[0, a:b, heads]),
+        ro, state = oracle_recurrent(cut(p.q), cut(p.k), cut(p.v), cut(p.g), host64(p.beta[0, a:b, heads]),
                                      S0=state)
         got = host64(o[0, a:b, heads])
         err_max = max(err_max, float(np.abs(got - ro).max()))

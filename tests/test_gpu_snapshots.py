@@ -12,9 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from gated_delta_rule_103_amd import inputs, kda_prefill, kda_prefill_snapshots
-from kda_testlib import TOL_BF16, TOL_F32, host64, rel_err, to_dev
+from kda_testlib import TOL_BF16, TOL_F32, host64, oracle_recurrent, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +57,7 @@ def _check(p, every, max_snaps, tol, label):
                 assert np.isnan(sn[n, :, slot]).all(), (n, slot)
                 continue
             a, b = int(cu[n]), int(cu[n]) + t
-            _, ref = oracle.recurrent(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b],
+            _, ref = oracle_recurrent(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b],
                                       S0=None if s0 is None else s0[n:n + 1])
             e = rel_err(sn[n, :, slot], ref[0])
             assert e <= tol["S"], (n, slot, e)

@@ -17,10 +17,9 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from gated_delta_rule_103_amd import gdn_prefill, inputs, kda_prefill, kda_prefill_snapshots
 from gated_delta_rule_103_amd.kda import kda_prefill_workspace_size
-from kda_testlib import TOL_BF16, host64, oracle_prefill, rel_err, to_dev
+from kda_testlib import TOL_BF16, host64, oracle_prefill, oracle_recurrent, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -150,7 +149,7 @@ def test_windowed_snapshots_across_window_borders():
         if b > T_LONG:
             assert np.isnan(sn[0, :, slot]).all(), slot
             continue
-        _, state = oracle.recurrent(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], S0=state,
+        _, state = oracle_recurrent(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], S0=state,
                                     cu_seqlens=np.array([0, b - a], dtype=np.int64))
         e = rel_err(sn[0, :, slot], state[0])
         say(f"    slot {slot} (token {b}): err {e:.3e}")
