@@ -125,7 +125,8 @@ struct Rec {
 
 // ---------------------------------------------------------------- prep
 template <int N> struct IC { static constexpr int value = N; };    // an int as a type (compile-time argument)
-constexpr int PTHR = 512;        // prep: 8 wavefronts, two per SIMD to hide latency
+constexpr int PTHR = 768;        // prep: 12 wavefronts, three per SIMD to hide latency:
+constexpr int PWORK = 512;       // wavefronts 0-7 take an item's main work, 8-11 help (below)
 constexpr int SQ = D + 8;        // bf16 row stride of q, k           [64][136]
 constexpr int SE = D + 4;        // fp32 row stride of the decays     [64][132]
 constexpr int SL = C + 4;        // fp32 row stride of L / INV^T      [64][68]
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         if (part <= 0) {
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
-                const int idx = tid0 + it * PTHR, row = idx >> 4, part = idx & 15;
+                const int idx = tid0 + it * PWORK, row = idx >> 4, part = idx & 15;
                 const size_t off = ((size_t)(tok0 + min(row, Lc - 1)) * H + h) * D + 8 * part;
                 rq[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.q + off));
                 rk[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k + off));
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // ================= stage q and k in LDS (rows past the end: zeros, alpha = 1)
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int idx = tid + it * PTHR, row = idx >> 4, part = idx & 15;
+            const int idx = tid + it * PWORK, row = idx >> 4, part = idx & 15;
             const u32x4 z0 = {0u, 0u, 0u, 0u};
             *reinterpret_cast<u32x4 *>(sQs + row * SQ + 8 * part) = row < Lc ? rq[it] : z0;
             *reinterpret_cast<u32x4 *>(sKs + row * SQ + 8 * part) = row < Lc ? rk[it] : z0;
@@ -493,40 +494,6 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             else if (wave == 5) offdiag(IC<3>{}, IC<2>{}, IC<1>{});
             else if (wave == 6) offdiag(IC<2>{}, IC<0>{}, IC<2>{});
             else offdiag(IC<1>{}, IC<0>{}, IC<1>{});
-            // Kr = KF H for the 16 tokens of block I = wave - 4, written channel-major
-            // (Kr^T) so that the record's Kr^T fragments are single 16-byte reads. A
-            // lane takes a token pair (16I + 2(lane & 7), +1) and eight-channel groups
-            // lane >> 3 and (lane >> 3) + 8, and writes each (channel, token pair) as
-            // one dword.
-            {
-                const int I = wave & 3;
-                const int t0 = 16 * I + 2 * (lane & 7);
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    const int c0 = 8 * ((lane >> 3) + 8 * gg);
-                    // H (block I end -> chunk end) = product of the later block decays
-                    f32x4 h0 = {1.f, 1.f, 1.f, 1.f}, h1 = h0;
-#pragma unroll
-                    for (int K = 1; K < 4; ++K)
-                        if (K > I) {                                      // uniform
-                            h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
-                            h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
-                        }
-                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0);
-                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0 + 4);
-                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0);
-                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0 + 4);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float hh = e < 4 ? h0[e] : h1[e - 4];
-                        const float xa = (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
-                        const float xb = (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
-                        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-                        const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
-                        *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
-                    }
-                }
-            }
         }
         // exact path for diagonal blocks whose in-block decay leaves the fp32 normal range
         for (int I = 0; I < 4 && (flags.x | flags.y | flags.z | flags.w); ++I) {
@@ -595,27 +562,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // the flags were read above (into registers); clear them for the next item
         if (tid < 4) sFlag[tid] = 0;
 
-        // ================= INV = (I + L)^{-1} off the diagonal blocks, and record fragments
-        // Waves 0-3 take their Kr^T record fragments and form the off-diagonal
-        // blocks of INV; waves 4-7 (token tile tt = wave - 4) build Kd^T for the W
-        // product (into LDS, over the F tile, which is dead now) and their Qd and
-        // Mqk record fragments. Every record fragment is held in registers until
-        // the record is stored.
-        f16x8 fr[8];
-        if (wave < 4) {
-            // Kr^T record fragments: rows = channels 32w + 16rt + l16, k = tokens of
-            // U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); Kr^T is final
-            typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const _Float16 *row = sKrt + (32 * wave + 16 * rt + l16) * SKR + 32 * ks + 4 * lq;
-                    const f16x4_ a = *reinterpret_cast<const f16x4_ *>(row);
-                    const f16x4_ b = *reinterpret_cast<const f16x4_ *>(row + 16);
-                    fr[2 * rt + ks] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-                }
-        } else {
+        // ================= INV = (I + L)^{-1} off the diagonal blocks, and Kd^T
+        // Waves 0-3 form the off-diagonal blocks of INV; waves 4-7 (token tile
+        // tt = wave - 4) build Kd^T for the W product (into LDS, over the F tile,
+        // which is dead now). The helpers build and store the Qd and Mqk record
+        // fragments meanwhile.
+        if (wave >= 4) {
             const int tt = wave & 3;
             // Kd^T = (k e^{a})^T = (KE G)^T, channel-major: a lane takes a token pair
             // (16 tt + 2 (lane & 7), +1) and eight-channel groups lane >> 3 and
@@ -722,54 +674,18 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             if (wave == 3)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sLI[(32 + 4 * lq + i) * SL + 48 + l16] = inv32t[i];  // INV_32
-        } else {
-            const int tt = wave & 3;
-            // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
-            // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
-            // 32w + 16 + 4lq + {0..3})
-            {
-                const int t = 16 * tt + l16;
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int c0 = 32 * w + 16 * hh + 4 * lq;
-                        const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
-                        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
-                    }
-            }
-            // strictly lower Mqk for token tile tt in the scan's token order of U
-            // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
-            // the diagonal block are never written and are selected as zeros (a
-            // select, so stale LDS contents cannot leak in)
-            {
-                const int t = 16 * tt + l16;
-                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
-                        const bool zero = 2 * ks + hh > tt;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
-                    }
-            }
         }
         __syncthreads();
         fetch(next, 2);
 
         // ================= record: fp16 fragments of the scan's operands
-        // Wavefront p: token tile tt = p & 3. Waves 0-3 (scan wavefront w = p)
-        // build Kr^T and IB here; waves 4-7 built Qd and Mqk above. Every wave
-        // builds the IB fragments of its token tile, which are also the right
-        // operand of W^T = Kd^T IB^T, and forms W for the channel tiles
-        // 4 (p >> 2) .. +3 (scan wavefronts 2 (p >> 2) and 2 (p >> 2) + 1).
-        // Both roles then store eight fragments from the same code: stores
-        // inside role branches would leave the compiler a path without them, and
-        // its wait for the next item's inputs would then also wait for the stores.
+        // Wavefront p: token tile tt = p & 3. Every wave builds the IB fragments of
+        // its token tile, which are also the right operand of W^T = Kd^T IB^T, and
+        // forms W for the channel tiles 4 (p >> 2) .. +3 (scan wavefronts 2 (p >> 2)
+        // and 2 (p >> 2) + 1). Waves 0-3 store their IB fragments and one Kr^T
+        // fragment, waves 4-7 three Kr^T fragments: five stores on either path (a
+        // path with fewer stores than the other would make the compiler's wait for
+        // the next item's inputs also wait for stores).
         {
             const int tt = wave & 3;
             const int t = 16 * tt + l16;
@@ -788,10 +704,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     ib[ks][e] = static_cast<_Float16>(sc <= t ? x : 0.f);
                 }
             }
-            if (wave < 4) {
-                fr[4] = ib[0];
-                fr[5] = ib[1];
-            }
+            f16x8 wf[2];
             // W^T tiles (channels 16 ct .. +15) x (tokens of tile tt): Kd^T rows times
             // IB^T; IB is lower triangular, so token tiles 0 and 1 need only the first
             // 32 tokens. Output layout: lane (token t, channels 16ct + 4lq + {0..3}),
@@ -800,6 +713,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             {
                 const int ct0 = 4 * (wave >> 2);
                 f32x4 acc[4];
+                static_assert(PWORK == 512, "eight main wavefronts: channel tiles 0-7");
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -814,29 +728,38 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) fr[6 + j][e] = static_cast<_Float16>(-acc[2 * j + (e >> 2)][e & 3]);
+                    for (int e = 0; e < 8; ++e) wf[j][e] = static_cast<_Float16>(-acc[2 * j + (e >> 2)][e & 3]);
             }
-            // fragment i of wave p goes to (scan wavefront, byte offset in its part):
-            //   waves 0-3: Kr 0-3 -> (p, KR + i KB); IB 4-5 -> (p, IB + (i - 4) KB)
-            //   waves 4-7: Qd 0-3 -> (i, QD + tt KB); Mqk 4-5 -> (tt, MQ + (i - 4) KB)
-            //   both: W 6-7 -> (2 (p >> 2) + i - 6, NW + tt KB)
+            // Kr^T fragment (rt, ks) of scan wavefront w: rows = channels 32w + 16rt +
+            // l16, k = tokens of U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3})
+            auto kr_frag = [&](int w, int rt, int ks) {
+                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
+                const _Float16 *row = sKrt + (32 * w + 16 * rt + l16) * SKR + 32 * ks + 4 * lq;
+                const f16x4_ a = *reinterpret_cast<const f16x4_ *>(row);
+                const f16x4_ b = *reinterpret_cast<const f16x4_ *>(row + 16);
+                return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            };
+            // (scan wavefront, byte offset in its part) of every fragment:
+            //   waves 0-3: Kr (p, 0, 0) -> (p, KR); IB ks -> (p, IB + ks KB)
+            //   waves 4-7: Kr (p - 4, rt, ks) for (0, 1), (1, 0), (1, 1) -> (p - 4, KR + (2 rt + ks) KB)
+            //   both: W j -> (2 (p >> 2) + j, NW + tt KB)
             static_assert(Rec::IB == Rec::KR + 4096, "record layout");
             char *rec = p.rec + ((size_t)h * p.rec_stride + ci - p.cw0) * Rec::BYTES + lane * 16;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int w_s, off;
-                if (i >= 6) {
-                    w_s = 2 * (wave >> 2) + i - 6;
-                    off = Rec::NW + tt * 1024;
-                } else if (wave < 4) {
-                    w_s = wave;
-                    off = Rec::KR + i * 1024;
-                } else {
-                    w_s = i < 4 ? i : tt;
-                    off = i < 4 ? Rec::QD + tt * 1024 : Rec::MQ + (i - 4) * 1024;
-                }
-                __builtin_nontemporal_store(fr[i], reinterpret_cast<f16x8 *>(rec + (size_t)w_s * Rec::WAVE + off));
+            auto put = [&](f16x8 x, int w_s, int off) {
+                __builtin_nontemporal_store(x, reinterpret_cast<f16x8 *>(rec + (size_t)w_s * Rec::WAVE + off));
+            };
+            if (wave < 4) {
+                put(kr_frag(wave, 0, 0), wave, Rec::KR);
+                put(ib[0], wave, Rec::IB);
+                put(ib[1], wave, Rec::IB + 1024);
+            } else {
+                const int w = wave & 3;
+                put(kr_frag(w, 0, 1), w, Rec::KR + 1024);
+                put(kr_frag(w, 1, 0), w, Rec::KR + 2048);
+                put(kr_frag(w, 1, 1), w, Rec::KR + 3072);
             }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) put(wf[j], 2 * (wave >> 2) + j, Rec::NW + tt * 1024);
             // d (64 floats) then gamma (128 floats): one float per thread, every
             // thread issues the store and the range check drops those past the end
             static_assert(Rec::GAM == Rec::DG + C * 4, "record layout");
@@ -850,6 +773,99 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     };
     if (tid0 < 4) sFlag[tid0] = 0;
     __syncthreads();
+    if (wave >= 8) {
+        // Helper wavefronts 8-11 (block and token tile wave - 8), through the same
+        // five barriers per item as the main ones: Kr^T of their block during the
+        // L / Mqk phase, then the Qd and Mqk record fragments of their token tile,
+        // built and stored during the inverse phase.
+        const int lane = tid0 & 63, l16 = lane & 15, lq = lane >> 4;
+        for (int item = blockIdx.x; item < items; item += gridDim.x) {
+            const int ci = chunk_of(item), h = item % H;
+            __syncthreads();                             // stage and decays
+            __syncthreads();                             // decayed tiles
+            // Kr = KF H for the 16 tokens of block I = wave - 8, written channel-major
+            // (Kr^T) so that the record's Kr^T fragments are single 16-byte reads. A
+            // lane takes a token pair (16I + 2(lane & 7), +1) and eight-channel groups
+            // lane >> 3 and (lane >> 3) + 8, and writes each (channel, token pair) as
+            // one dword.
+            {
+                const int I = wave & 3;
+                const int t0 = 16 * I + 2 * (lane & 7);
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int c0 = 8 * ((lane >> 3) + 8 * gg);
+                    // H (block I end -> chunk end) = product of the later block decays
+                    f32x4 h0 = {1.f, 1.f, 1.f, 1.f}, h1 = h0;
+#pragma unroll
+                    for (int K = 1; K < 4; ++K)
+                        if (K > I) {                                      // uniform
+                            h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
+                            h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
+                        }
+                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0);
+                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0 + 4);
+                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0);
+                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float hh = e < 4 ? h0[e] : h1[e - 4];
+                        const float xa = (e < 4 ? fa0[e] : fa1[e - 4]) * hh;
+                        const float xb = (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
+                        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+                        const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
+                        *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
+                    }
+                }
+            }
+            __syncthreads();                             // L / Mqk, diagonal inverse
+            {
+                f16x8 fr[6];
+                const int tt = wave & 3;
+                // Qd = q e^{a} = QE G for token tile tt, one fragment per scan wavefront w,
+                // in that wavefront's state-channel order (channels 32w + 4lq + {0..3},
+                // 32w + 16 + 4lq + {0..3})
+                {
+                    const int t = 16 * tt + l16;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int c0 = 32 * w + 16 * hh + 4 * lq;
+                            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
+                            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
+                        }
+                }
+                // strictly lower Mqk for token tile tt in the scan's token order of U
+                // (tokens 32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3}); blocks above
+                // the diagonal block are never written and are selected as zeros (a
+                // select, so stale LDS contents cannot leak in)
+                {
+                    const int t = 16 * tt + l16;
+                    typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const f16x4_ mq = *reinterpret_cast<const f16x4_ *>(sMqk + t * SMQ + 32 * ks + 16 * hh + 4 * lq);
+                            const bool zero = 2 * ks + hh > tt;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) fr[4 + ks][4 * hh + i] = zero ? static_cast<_Float16>(0.f) : mq[i];
+                        }
+                }
+                // Qd w -> (w, QD + tt KB); Mqk ks -> (tt, MQ + ks KB)
+                char *rec = p.rec + ((size_t)h * p.rec_stride + ci - p.cw0) * Rec::BYTES + lane * 16;
+#pragma unroll
+                for (int i = 0; i < 6; ++i)
+                    __builtin_nontemporal_store(fr[i], reinterpret_cast<f16x8 *>(
+                        rec + (size_t)(i < 4 ? i : tt) * Rec::WAVE + (i < 4 ? Rec::QD + tt * 1024 : Rec::MQ + (i - 4) * 1024)));
+            }
+            __syncthreads();                             // off-diagonal inverse
+            __syncthreads();                             // record
+        }
+        return;
+    }
     if ((int)blockIdx.x < items) {
         fetch(blockIdx.x, -1);
         body(blockIdx.x);
