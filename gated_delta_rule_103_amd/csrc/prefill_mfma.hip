@@ -224,6 +224,34 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     // (256 MB) when the whole set is larger.
     auto chunk_of = [&](int item) { return p.cw0 + wn - 1 - item / H; };
 
+    // X_I (KF_I / Gamma_I)^T for diagonal block I on fp32 MFMA (X = KE gives L's
+    // block, X = QE Mqk's): lane (l16, lq) gets rows 16I + 4lq + i of column
+    // 16I + l16, over the 128 channels in four k-steps of 32; four partial sums
+    // (k-slot e & 3) make four independent MFMA chains.
+    auto diag_product = [&](const float *sX, int I, int lane) {
+        const int l16 = lane & 15, lq = lane >> 4, t = 16 * I + l16;
+        f32x4 a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            // lane: row / column t, channels 32ks + 8lq + e; product e contracts
+            // channels 32ks + 8j + e over the four k-slots j
+            const int c0 = 32 * ks + 8 * lq;
+            f32x4 x[2], bk[2];
+#pragma unroll
+            for (int hv = 0; hv < 2; ++hv) {
+                x[hv] = *reinterpret_cast<const f32x4 *>(sX + t * SE + c0 + 4 * hv);
+                bk[hv] = *reinterpret_cast<const f32x4 *>(sKF + t * SE + c0 + 4 * hv) *
+                         *reinterpret_cast<const f32x4 *>(sIGB + I * D + c0 + 4 * hv);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a[e & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e >> 2][e & 3], bk[e >> 2][e & 3], a[e & 3], 0, 0, 0);
+        }
+        return (a[0] + a[1]) + (a[2] + a[3]);
+    };
+
     // Inputs of one (chunk, head) item, fetched one item ahead, and the record
     // stores, carry the non-temporal hint (each byte is touched once here; the
     // hint keeps them from displacing lines the scan still reads). The loads are
@@ -385,56 +413,31 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 
         // ================= L and Mqk on MFMA, the 10 16x16 blocks with I >= J
         // Left operands x_t E_t (KE for L, QE for Mqk), t in block I.
-        // Diagonal blocks (wavefronts 0-3, I = J = wavefront): right operands
-        // k_s / E_s = KF_s / Gamma_I (start of block as reference, bounded by
-        // 1 / Gamma_I; a block with Gamma_I below FLT_MIN takes the exact path
-        // instead), multiplied in fp32 on v_mfma_f32_16x16x4f32: near-diagonal
-        // entries dominate o, and fp32 operands need no hi/lo splitting.
+        // Diagonal blocks (L's on wavefronts 0-3, I = J = wavefront; Mqk's on the
+        // helper wavefronts 8-11): right operands k_s / E_s = KF_s / Gamma_I (start
+        // of block as reference, bounded by 1 / Gamma_I; a block with Gamma_I below
+        // FLT_MIN takes the exact path instead), multiplied in fp32 on
+        // v_mfma_f32_16x16x4f32: near-diagonal entries dominate o, and fp32
+        // operands need no hi/lo splitting.
         // Off-diagonal blocks (wavefronts 4-7): right operands KF_s
         // prod_{J<K<I} Gamma_K; every factor is <= 1, so both operands are rounded
         // once to fp16 (11-bit significand) and multiplied on fp16 MFMA. A wave's
         // blocks share their row block, so its left operands are built once.
         //   wavefront 4: (3,0) (3,1)   5: (3,2)   6: (2,0) (2,1)   7: (1,0)
-        // Then waves 4-7 form Kr^T of block wave - 4, and waves 0-3 invert their
-        // diagonal block of I + L.
+        // Then waves 0-3 invert their diagonal block of I + L (the helpers form
+        // Kr^T meanwhile).
         // the four flags in one LDS read (a serial read per block cost a round trip each)
         const int4 flags = *reinterpret_cast<const int4 *>(sFlag);
         if (wave < 4) {
             const int I = wave;
             if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) {
-                const int t = 16 * I + l16;
-                // two partial sums per product (even and odd k-slots), so that four
-                // independent MFMA chains fill the pipe
-                f32x4 aL[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, aM[2] = {aL[0], aL[0]};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    // lane: row / column t, channels 32ks + 8lq + e; product e contracts
-                    // channels 32ks + 8j + e over the four k-slots j
-                    const int c0 = 32 * ks + 8 * lq;
-                    f32x4 ke[2], qe[2], bk[2];
-#pragma unroll
-                    for (int hv = 0; hv < 2; ++hv) {
-                        ke[hv] = *reinterpret_cast<const f32x4 *>(sKE + t * SE + c0 + 4 * hv);
-                        qe[hv] = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0 + 4 * hv);
-                        bk[hv] = *reinterpret_cast<const f32x4 *>(sKF + t * SE + c0 + 4 * hv) *
-                                 *reinterpret_cast<const f32x4 *>(sIGB + I * D + c0 + 4 * hv);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        aL[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(ke[e >> 2][e & 3], bk[e >> 2][e & 3], aL[e & 1], 0, 0, 0);
-                        aM[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qe[e >> 2][e & 3], bk[e >> 2][e & 3], aM[e & 1], 0, 0, 0);
-                    }
-                }
-                const f32x4 accL = aL[0] + aL[1], accM = aM[0] + aM[1];
+                // L's block; the helper wavefront on the same SIMD forms Mqk's
+                const f32x4 accL = diag_product(sKE, I, lane);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
-                    const bool lower = sc < tr;
                     // masked entries may hold inf / nan: select, do not scale
-                    if (lower) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
-                    sMqk[tr * SMQ + sc] = static_cast<_Float16>(lower ? accM[i] : 0.f);
-                    // the diagonal is d_t = q_t . k_t: (q_t E_t)(k_t F_t / Gamma_I) in fp32
-                    if (sc == tr) sDg[tr] = accM[i];
+                    if (sc < tr) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
                 }
             }
         } else {
@@ -783,6 +786,23 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const int ci = chunk_of(item), h = item % H;
             __syncthreads();                             // stage and decays
             __syncthreads();                             // decayed tiles
+            // Mqk's diagonal block I = wave - 8 (strictly lower part, zeros on and
+            // above the diagonal) and d_t = q_t . k_t, its diagonal: (q_t E_t)(k_t F_t /
+            // Gamma_I) in fp32. A block on the exact path is left to its diagonal
+            // wavefront.
+            {
+                const int4 flags = *reinterpret_cast<const int4 *>(sFlag);
+                const int I = wave & 3;
+                if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) {
+                    const f32x4 accM = diag_product(sQE, I, lane);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
+                        sMqk[tr * SMQ + sc] = static_cast<_Float16>(sc < tr ? accM[i] : 0.f);
+                        if (sc == tr) sDg[tr] = accM[i];
+                    }
+                }
+            }
             // Kr = KF H for the 16 tokens of block I = wave - 8, written channel-major
             // (Kr^T) so that the record's Kr^T fragments are single 16-byte reads. A
             // lane takes a token pair (16I + 2(lane & 7), +1) and eight-channel groups
