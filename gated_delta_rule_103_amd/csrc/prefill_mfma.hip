@@ -14,8 +14,10 @@
 //     O     = Qd M + Mqk U
 //     M_out = Diag(gamma) M + Kr^T U
 //
-// prep  (persistent, one workgroup per CU walking the (chunk, head) items,
-//       all chunks in parallel): decays as products of alpha = exp(g) inside
+// prep  (persistent, one workgroup of twelve wavefronts per CU walking the
+//       (chunk, head) items, all chunks in parallel; eight take an item's main
+//       work, four help with Mqk's diagonal blocks, Kr^T and the Qd / Mqk
+//       record fragments): decays as products of alpha = exp(g) inside
 //       16-token blocks; L and Mqk with the diagonal 16x16 blocks on fp32
 //       MFMA and the off-diagonal ones on fp16 MFMA (every factor <= 1 there);
 //       the unit-lower-triangular inverse by substitution on the diagonal
