@@ -922,9 +922,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 // exactly (powers of two), and o, S_out and snapshots are scaled back.
 constexpr int NREC = 256;                // recurrence wavefronts, one per SIMD ...
 constexpr int SCAN_THR = 2 * NREC;       // ... and as many output wavefronts
-constexpr int SMS = D + 8;               // fp16 row stride of the state       [col][136]
-constexpr int SUS = C + 8;               // fp16 row stride of U               [col][72]
-constexpr int SVT = C + 8;               // bf16 row stride of the V tile      [col][72]
+// LDS tiles are [col][k] rows of 16-byte blocks, the block index XOR-ed with
+// the row: an MFMA operand read (16 lanes per bank cycle, 64 banks) then takes
+// 16 rows at one block index from 16 distinct bank groups. Measured on gfx950,
+// a plain padded row stride costs one extra cycle per 16 lanes on these reads.
+constexpr int SMS = D;                   // fp16 row of the state   [col][128], blocks ^ (col & 15)
+constexpr int SUS = C;                   // fp16 row of U           [col][64],  blocks ^ (col & 7)
+constexpr int SVT = C;                   // bf16 row of the V tile  [col][64],  blocks ^ (col & 7)
 
 template <int TV>
 struct ScanLds {
@@ -1020,10 +1024,14 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     const int r_lane = lane * 16;
     // B-operand fragments from LDS: the state's k-step kk (channels of
     // recurrence wavefront kk), U's token k-step ks
-    auto m_frag = [&](const _Float16 *base, int nt, int kk) { return lds8h(base + (16 * nt + l16) * SMS + 32 * kk + 8 * lq); };
-    auto u_frag = [&](const _Float16 *base, int nt, int ks) { return lds8h(base + (16 * nt + l16) * SUS + 32 * ks + 8 * lq); };
+    auto m_frag = [&](const _Float16 *base, int nt, int kk) {
+        return lds8h(base + (16 * nt + l16) * SMS + 8 * ((4 * kk + lq) ^ l16));
+    };
+    auto u_frag = [&](const _Float16 *base, int nt, int ks) {
+        return lds8h(base + (16 * nt + l16) * SUS + 8 * ((4 * ks + lq) ^ (l16 & 7)));
+    };
     // U's position for token 16tt + 4lq + i: 32 (tt >> 1) + 8lq + 4 (tt & 1) + i
-    const int u_at = (l16 * SUS) + 32 * (w4 >> 1) + 8 * lq + 4 * (w4 & 1);
+    const int u_at = (l16 * SUS) + 8 * ((4 * (w4 >> 1) + lq) ^ (l16 & 7)) + 4 * (w4 & 1);
 
     if (wave < 4) {
         // ============================ recurrence
@@ -1063,7 +1071,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
                     f16x4 hi, lo;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) SPLITH(Macc[rt][nt][i], hi[i], lo[i]);
-                    const int at = (16 * nt + l16) * SMS + 32 * w4 + 8 * lq + 4 * rt;
+                    const int at = (16 * nt + l16) * SMS + 8 * ((4 * w4 + lq) ^ l16) + 4 * rt;
                     *reinterpret_cast<f16x4 *>(sMh + at) = hi;
                     *reinterpret_cast<f16x4 *>(sMl + at) = lo;
                 }
@@ -1099,7 +1107,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8 vv = lds8(reinterpret_cast<const __bf16 *>(sV) + bsel * TV * SVT + (16 * nt + l16) * SVT +
-                                           32 * ks + 8 * lq);
+                                           8 * ((4 * ks + lq) ^ (l16 & 7)));
                     f16x8 vb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) vb[e] = static_cast<_Float16>(bf2f(vv[e]) * sc);
@@ -1270,13 +1278,15 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     // V of a chunk into LDS buffer bsel, transposed to [col][token], and this
     // wavefront's max |v| of it into slot bsel
     auto stage_v = [&](const OFrags &f, int bsel) {
-        bf16_t *dst = sV + bsel * TV * SVT + ((TV / 4) * (stid & 3)) * SVT + (stid >> 2);
+        const int t = stid >> 2, c0 = (TV / 4) * (stid & 3);
+        bf16_t *dst = sV + bsel * TV * SVT + (t & 7);
         float vm = 0.f;
 #pragma unroll
         for (int e = 0; e < 2 * VW; ++e) {
             const uint32_t wv = f.vr[e >> 1];
             const bf16_t x = static_cast<bf16_t>(e & 1 ? wv >> 16 : wv & 0xffffu);
-            dst[e * SVT] = x;
+            const int c = c0 + e;
+            dst[c * SVT + 8 * ((t >> 3) ^ (c & 7))] = x;
             vm = fmaxf(vm, fabsf(bf16_to_f32(x)));
         }
         vm = wave_max(vm);
