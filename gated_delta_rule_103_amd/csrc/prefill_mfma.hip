@@ -130,21 +130,29 @@ template <int N> struct IC { static constexpr int value = N; };    // an int as 
 constexpr int PTHR = 768;        // prep: 12 wavefronts, three per SIMD to hide latency:
 constexpr int PWORK = 512;       // wavefronts 0-7 take an item's main work, 8-11 help (below)
 constexpr int SQ = D + 8;        // bf16 row stride of q, k           [64][136]
-constexpr int SE = D + 4;        // fp32 row stride of the decays     [64][132]
 constexpr int SL = C + 4;        // fp32 row stride of L / INV^T      [64][68]
 constexpr int SMQ = C + 8;       // fp16 row stride of Mqk            [64][72]
-constexpr int SKR = C + 8;       // fp16 row stride of Kr^T           [128][72]
+// The decayed tiles (fp32 [64][128]) and Kr^T / Kd^T (fp16 [128][64]) are not
+// padded; their 16-byte blocks are XOR-ed with a function of the row instead,
+// chosen by measuring the bank-conflict counter of every access pattern of the
+// kernel on gfx950 (operand reads of 16 rows at one block, the channel-major
+// writes of the transposes): all of them are then conflict-free but the
+// transposes' row-pair reads (half as many conflict cycles as before).
+__device__ __forceinline__ int e_at(int t, int c) { return t * D + (c ^ ((t & 15) << 2)); }
+__device__ __forceinline__ int kt_at(int ch, int t) {
+    return ch * C + (t ^ ((((ch & 7) ^ (5 * (ch >> 3))) & 7) << 3));
+}
 
-// The decayed operand tiles, formed once per item (fp32 [64][SE], the L2 norm
+// The decayed operand tiles, formed once per item (fp32 [64][128], the L2 norm
 // of q and k applied when requested): KE = k E and QE = q E (E: the in-block
 // prefix decay, block start -> token), KF = k F (F: the in-block suffix decay,
 // token -> block end). Every operand of the products is one of them times at
 // most one per-channel factor.
 struct PrepLds {
     static constexpr int KE = 0;
-    static constexpr int QE = KE + C * SE * 4;
-    static constexpr int KF = QE + C * SE * 4;
-    static constexpr int LI = KF + C * SE * 4;       // fp32 L (strictly lower) and INV^T (upper, with diagonal)
+    static constexpr int QE = KE + C * D * 4;
+    static constexpr int KF = QE + C * D * 4;
+    static constexpr int LI = KF + C * D * 4;        // fp32 L (strictly lower) and INV^T (upper, with diagonal)
     static constexpr int MQK = LI + C * SL * 4;      // fp16 strictly lower Mqk
     static constexpr int DG = MQK + C * SMQ * 2;     // fp32 [64]
     static constexpr int BETA = DG + C * 4;          // fp32 [64]
@@ -155,13 +163,13 @@ struct PrepLds {
     static constexpr int RQ = GAM + D * 4;           // fp32 [64] 1 / ||q_t|| (L2-normalised input)
     static constexpr int RK = RQ + C * 4;            // fp32 [64] 1 / ||k_t||
     static constexpr int FLAG = RK + C * 4;          // int [4]
-    static constexpr int KRT = FLAG + 16;            // fp16 [128][SKR] Kr^T, channel-major
-    static constexpr int SIZE = KRT + D * SKR * 2;
+    static constexpr int KRT = (FLAG + 16 + 255) / 256 * 256;   // fp16 [128][64] Kr^T, channel-major
+    static constexpr int SIZE = KRT + (D * C > C * SQ ? D * C : C * SQ) * 2;
     // the bf16 rows of q and k are staged in the L and Kr^T tiles, free until the
     // decayed tiles have been formed
     static constexpr int QS = LI, KS = KRT;
 };
-static_assert(C * SQ * 2 <= C * SL * 4 && C * SQ * 2 <= D * SKR * 2, "q, k staging");
+static_assert(C * SQ * 2 <= C * SL * 4, "q staging");
 
 struct PrepParams {
     const bf16_t *q, *k;
@@ -212,9 +220,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     float *sRK = reinterpret_cast<float *>(smem + Lo::RK);
     int *sFlag = reinterpret_cast<int *>(smem + Lo::FLAG);
     _Float16 *sKrt = reinterpret_cast<_Float16 *>(smem + Lo::KRT);
-    // Kd^T [128][SKR] fp16, channel-major, built over the KF tile once it is dead
+    // Kd^T [128][64] fp16, channel-major, built over the KF tile once it is dead
     _Float16 *sKdT = reinterpret_cast<_Float16 *>(smem + Lo::KF);
-    static_assert(D * SKR * 2 <= C * SE * 4, "Kd^T fits over the KF tile");
+    static_assert(D * C * 2 <= C * D * 4, "Kd^T fits over the KF tile");
 
     const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // 8 wavefronts
     const int H = p.H;
@@ -243,8 +251,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             f32x4 x[2], bk[2];
 #pragma unroll
             for (int hv = 0; hv < 2; ++hv) {
-                x[hv] = *reinterpret_cast<const f32x4 *>(sX + t * SE + c0 + 4 * hv);
-                bk[hv] = *reinterpret_cast<const f32x4 *>(sKF + t * SE + c0 + 4 * hv) *
+                x[hv] = *reinterpret_cast<const f32x4 *>(sX + e_at(t, c0 + 4 * hv));
+                bk[hv] = *reinterpret_cast<const f32x4 *>(sKF + e_at(t, c0 + 4 * hv)) *
                          *reinterpret_cast<const f32x4 *>(sIGB + I * D + c0 + 4 * hv);
             }
 #pragma unroll
@@ -407,9 +415,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const int t = 16 * bI + tt;
             const float kk = NORM ? bf2f(sKs[t * SQ + bc]) * sRK[t] : bf2f(sKs[t * SQ + bc]);
             const float qq = NORM ? bf2f(sQs[t * SQ + bc]) * sRQ[t] : bf2f(sQs[t * SQ + bc]);
-            sKE[t * SE + bc] = kk * ev[tt];
-            sQE[t * SE + bc] = qq * ev[tt];
-            sKF[t * SE + bc] = kk * fv[tt];
+            sKE[e_at(t, bc)] = kk * ev[tt];
+            sQE[e_at(t, bc)] = qq * ev[tt];
+            sKF[e_at(t, bc)] = kk * fv[tt];
         }
         __syncthreads();
 
@@ -455,10 +463,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int c0 = 32 * ks + 8 * lq;
-                    const f32x4 ka0 = *reinterpret_cast<const f32x4 *>(sKE + t * SE + c0);
-                    const f32x4 ka1 = *reinterpret_cast<const f32x4 *>(sKE + t * SE + c0 + 4);
-                    const f32x4 qa0 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
-                    const f32x4 qa1 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0 + 4);
+                    const f32x4 ka0 = *reinterpret_cast<const f32x4 *>(sKE + e_at(t, c0));
+                    const f32x4 ka1 = *reinterpret_cast<const f32x4 *>(sKE + e_at(t, c0 + 4));
+                    const f32x4 qa0 = *reinterpret_cast<const f32x4 *>(sQE + e_at(t, c0));
+                    const f32x4 qa1 = *reinterpret_cast<const f32x4 *>(sQE + e_at(t, c0 + 4));
                     f16x8 aq, ak;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -468,8 +476,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int bb = 0; bb < NB; ++bb) {
                         const int J = bb ? 1 : J0, sr = 16 * J + l16;
-                        f32x4 b0 = *reinterpret_cast<const f32x4 *>(sKF + sr * SE + c0);
-                        f32x4 b1 = *reinterpret_cast<const f32x4 *>(sKF + sr * SE + c0 + 4);
+                        f32x4 b0 = *reinterpret_cast<const f32x4 *>(sKF + e_at(sr, c0));
+                        f32x4 b1 = *reinterpret_cast<const f32x4 *>(sKF + e_at(sr, c0 + 4));
                         // prod_{J<K<I} Gamma_K (none for adjacent blocks)
 #pragma unroll
                         for (int K = J + 1; K < I; ++K) {
@@ -586,10 +594,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     const int c0 = 8 * ((lane >> 3) + 8 * gg);
                     const f32x4 g0 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
                     const f32x4 g1 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0 + 4);
-                    const f32x4 ea0 = *reinterpret_cast<const f32x4 *>(sKE + t0 * SE + c0);
-                    const f32x4 ea1 = *reinterpret_cast<const f32x4 *>(sKE + t0 * SE + c0 + 4);
-                    const f32x4 eb0 = *reinterpret_cast<const f32x4 *>(sKE + (t0 + 1) * SE + c0);
-                    const f32x4 eb1 = *reinterpret_cast<const f32x4 *>(sKE + (t0 + 1) * SE + c0 + 4);
+                    const f32x4 ea0 = *reinterpret_cast<const f32x4 *>(sKE + e_at(t0, c0));
+                    const f32x4 ea1 = *reinterpret_cast<const f32x4 *>(sKE + e_at(t0, c0 + 4));
+                    const f32x4 eb0 = *reinterpret_cast<const f32x4 *>(sKE + e_at(t0 + 1, c0));
+                    const f32x4 eb1 = *reinterpret_cast<const f32x4 *>(sKE + e_at(t0 + 1, c0 + 4));
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float gg_ = e < 4 ? g0[e] : g1[e - 4];
@@ -597,7 +605,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         const float xb = (e < 4 ? eb0[e] : eb1[e - 4]) * gg_;
                         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
                         const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
-                        *reinterpret_cast<f16x2 *>(sKdT + (c0 + e) * SKR + t0) = pr;
+                        *reinterpret_cast<f16x2 *>(sKdT + kt_at(c0 + e, t0)) = pr;
                     }
                 }
             }
@@ -722,12 +730,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    acc[c] = mfma_f16(lds8h(sKdT + (16 * (ct0 + c) + l16) * SKR + 8 * lq), ib[0], acc[c]);
+                    acc[c] = mfma_f16(lds8h(sKdT + kt_at(16 * (ct0 + c) + l16, 8 * lq)), ib[0], acc[c]);
                 }
                 if (tt >= 2) {                                              // uniform
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        acc[c] = mfma_f16(lds8h(sKdT + (16 * (ct0 + c) + l16) * SKR + 32 + 8 * lq), ib[1], acc[c]);
+                        acc[c] = mfma_f16(lds8h(sKdT + kt_at(16 * (ct0 + c) + l16, 32 + 8 * lq)), ib[1], acc[c]);
                 }
                 // stored negated: the scan forms U = U~ + (-W) M
 #pragma unroll
@@ -739,9 +747,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             // l16, k = tokens of U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3})
             auto kr_frag = [&](int w, int rt, int ks) {
                 typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-                const _Float16 *row = sKrt + (32 * w + 16 * rt + l16) * SKR + 32 * ks + 4 * lq;
-                const f16x4_ a = *reinterpret_cast<const f16x4_ *>(row);
-                const f16x4_ b = *reinterpret_cast<const f16x4_ *>(row + 16);
+                const int ch = 32 * w + 16 * rt + l16;
+                const f16x4_ a = *reinterpret_cast<const f16x4_ *>(sKrt + kt_at(ch, 32 * ks + 4 * lq));
+                const f16x4_ b = *reinterpret_cast<const f16x4_ *>(sKrt + kt_at(ch, 32 * ks + 16 + 4 * lq));
                 return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
             };
             // (scan wavefront, byte offset in its part) of every fragment:
@@ -824,10 +832,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                             h0 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0);
                             h1 *= *reinterpret_cast<const f32x4 *>(sGB + K * D + c0 + 4);
                         }
-                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0);
-                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + t0 * SE + c0 + 4);
-                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0);
-                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + (t0 + 1) * SE + c0 + 4);
+                    const f32x4 fa0 = *reinterpret_cast<const f32x4 *>(sKF + e_at(t0, c0));
+                    const f32x4 fa1 = *reinterpret_cast<const f32x4 *>(sKF + e_at(t0, c0 + 4));
+                    const f32x4 fb0 = *reinterpret_cast<const f32x4 *>(sKF + e_at(t0 + 1, c0));
+                    const f32x4 fb1 = *reinterpret_cast<const f32x4 *>(sKF + e_at(t0 + 1, c0 + 4));
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float hh = e < 4 ? h0[e] : h1[e - 4];
@@ -835,7 +843,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         const float xb = (e < 4 ? fb0[e] : fb1[e - 4]) * hh;
                         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
                         const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
-                        *reinterpret_cast<f16x2 *>(sKrt + (c0 + e) * SKR + t0) = pr;
+                        *reinterpret_cast<f16x2 *>(sKrt + kt_at(c0 + e, t0)) = pr;
                     }
                 }
             }
@@ -853,7 +861,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                         for (int hh = 0; hh < 2; ++hh) {
                             const int c0 = 32 * w + 16 * hh + 4 * lq;
-                            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + t * SE + c0);
+                            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(sQE + e_at(t, c0));
                             const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + tt * D + c0);
 #pragma unroll
                             for (int i = 0; i < 4; ++i) fr[w][4 * hh + i] = static_cast<_Float16>(x4[i] * g4[i]);
