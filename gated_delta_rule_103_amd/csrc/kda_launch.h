@@ -76,7 +76,7 @@ hipError_t launch_chunk_plan(const int32_t *cu, int N, int C, int32_t *chunk_off
 size_t prefill_f32_workspace(int N, long long T_total, int H, int Dk, int Dv, int C);
 hipError_t launch_prefill_f32(const PrefillArgs &a);
 
-// bf16 MFMA chunked prefill.
+// MFMA chunked prefill for bf16 inputs (fp16 and fp32 MFMA, fp32 accumulation).
 size_t prefill_mfma_workspace(int N, long long T_total, int H, int Dk, int Dv, int C);
 hipError_t launch_prefill_mfma(const PrefillArgs &a);
 
