@@ -796,23 +796,9 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             const int ci = chunk_of(item), h = item % H;
             __syncthreads();                             // stage and decays
             __syncthreads();                             // decayed tiles
-            // Mqk's diagonal block I = wave - 8 (strictly lower part, zeros on and
-            // above the diagonal) and d_t = q_t . k_t, its diagonal: (q_t E_t)(k_t F_t /
-            // Gamma_I) in fp32. A block on the exact path is left to its diagonal
-            // wavefront.
-            {
-                const int4 flags = *reinterpret_cast<const int4 *>(sFlag);
-                const int I = wave & 3;
-                if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) {
-                    const f32x4 accM = diag_product(sQE, I, lane);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
-                        sMqk[tr * SMQ + sc] = static_cast<_Float16>(sc < tr ? accM[i] : 0.f);
-                        if (sc == tr) sDg[tr] = accM[i];
-                    }
-                }
-            }
+            // Kr^T first (vector ALU and LDS work, beside the MFMA products of the
+            // diagonal wavefronts), then Mqk's diagonal block (MFMA, beside their
+            // substitution, which is vector ALU work)
             // Kr = KF H for the 16 tokens of block I = wave - 8, written channel-major
             // (Kr^T) so that the record's Kr^T fragments are single 16-byte reads. A
             // lane takes a token pair (16I + 2(lane & 7), +1) and eight-channel groups
@@ -844,6 +830,23 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
                         const f16x2 pr = {static_cast<_Float16>(xa), static_cast<_Float16>(xb)};
                         *reinterpret_cast<f16x2 *>(sKrt + kt_at(c0 + e, t0)) = pr;
+                    }
+                }
+            }
+            // Mqk's diagonal block I = wave - 8 (strictly lower part, zeros on and
+            // above the diagonal) and d_t = q_t . k_t, its diagonal: (q_t E_t)(k_t F_t /
+            // Gamma_I) in fp32. A block on the exact path is left to its diagonal
+            // wavefront.
+            {
+                const int4 flags = *reinterpret_cast<const int4 *>(sFlag);
+                const int I = wave & 3;
+                if (!(I == 0 ? flags.x : I == 1 ? flags.y : I == 2 ? flags.z : flags.w)) {
+                    const f32x4 accM = diag_product(sQE, I, lane);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
+                        sMqk[tr * SMQ + sc] = static_cast<_Float16>(sc < tr ? accM[i] : 0.f);
+                        if (sc == tr) sDg[tr] = accM[i];
                     }
                 }
             }
