@@ -261,6 +261,15 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         }
         return (a[0] + a[1]) + (a[2] + a[3]);
     };
+    // Kr^T fragment (rt, ks) of scan wavefront w: rows = channels 32w + 16rt +
+    // l16, k = tokens of U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3})
+    auto kr_frag = [&](int w, int rt, int ks, int lane) {
+        typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
+        const int ch = 32 * w + 16 * rt + (lane & 15), lq = lane >> 4;
+        const f16x4_ a = *reinterpret_cast<const f16x4_ *>(sKrt + kt_at(ch, 32 * ks + 4 * lq));
+        const f16x4_ b = *reinterpret_cast<const f16x4_ *>(sKrt + kt_at(ch, 32 * ks + 16 + 4 * lq));
+        return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    };
 
     // Inputs of one (chunk, head) item, fetched one item ahead, and the record
     // stores, carry the non-temporal hint (each byte is touched once here; the
@@ -693,12 +702,12 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 
         // ================= record: fp16 fragments of the scan's operands
         // Wavefront p: token tile tt = p & 3. Every wave builds the IB fragments of
-        // its token tile, which are also the right operand of W^T = Kd^T IB^T, and
+        // its token tile, which are also the right operand of W^T = Kd^T IB^T,
         // forms W for the channel tiles 4 (p >> 2) .. +3 (scan wavefronts 2 (p >> 2)
-        // and 2 (p >> 2) + 1). Waves 0-3 store their IB fragments and one Kr^T
-        // fragment, waves 4-7 three Kr^T fragments: five stores on either path (a
-        // path with fewer stores than the other would make the compiler's wait for
-        // the next item's inputs also wait for stores).
+        // and 2 (p >> 2) + 1), and stores IB's token k-step p >> 2: three stores on
+        // every path (a path with fewer stores than another would make the
+        // compiler's wait for the next item's inputs also wait for stores). The
+        // helpers store the Kr^T fragments meanwhile.
         {
             const int tt = wave & 3;
             const int t = 16 * tt + l16;
@@ -743,34 +752,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) wf[j][e] = static_cast<_Float16>(-acc[2 * j + (e >> 2)][e & 3]);
             }
-            // Kr^T fragment (rt, ks) of scan wavefront w: rows = channels 32w + 16rt +
-            // l16, k = tokens of U's order (32ks + 4lq + {0..3}, 32ks + 16 + 4lq + {0..3})
-            auto kr_frag = [&](int w, int rt, int ks) {
-                typedef _Float16 f16x4_ __attribute__((ext_vector_type(4)));
-                const int ch = 32 * w + 16 * rt + l16;
-                const f16x4_ a = *reinterpret_cast<const f16x4_ *>(sKrt + kt_at(ch, 32 * ks + 4 * lq));
-                const f16x4_ b = *reinterpret_cast<const f16x4_ *>(sKrt + kt_at(ch, 32 * ks + 16 + 4 * lq));
-                return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-            };
             // (scan wavefront, byte offset in its part) of every fragment:
-            //   waves 0-3: Kr (p, 0, 0) -> (p, KR); IB ks -> (p, IB + ks KB)
-            //   waves 4-7: Kr (p - 4, rt, ks) for (0, 1), (1, 0), (1, 1) -> (p - 4, KR + (2 rt + ks) KB)
-            //   both: W j -> (2 (p >> 2) + j, NW + tt KB)
-            static_assert(Rec::IB == Rec::KR + 4096, "record layout");
+            //   IB ks = p >> 2 -> (tt, IB + ks KB);  W j -> (2 (p >> 2) + j, NW + tt KB)
             char *rec = p.rec + ((size_t)h * p.rec_stride + ci - p.cw0) * Rec::BYTES + lane * 16;
             auto put = [&](f16x8 x, int w_s, int off) {
                 __builtin_nontemporal_store(x, reinterpret_cast<f16x8 *>(rec + (size_t)w_s * Rec::WAVE + off));
             };
-            if (wave < 4) {
-                put(kr_frag(wave, 0, 0), wave, Rec::KR);
-                put(ib[0], wave, Rec::IB);
-                put(ib[1], wave, Rec::IB + 1024);
-            } else {
-                const int w = wave & 3;
-                put(kr_frag(w, 0, 1), w, Rec::KR + 1024);
-                put(kr_frag(w, 1, 0), w, Rec::KR + 2048);
-                put(kr_frag(w, 1, 1), w, Rec::KR + 3072);
-            }
+            put(wave >> 2 ? ib[1] : ib[0], tt, Rec::IB + (wave >> 2) * 1024);
 #pragma unroll
             for (int j = 0; j < 2; ++j) put(wf[j], 2 * (wave >> 2) + j, Rec::NW + tt * 1024);
             // d (64 floats) then gamma (128 floats): one float per thread, every
@@ -790,7 +778,8 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         // Helper wavefronts 8-11 (block and token tile wave - 8), through the same
         // five barriers per item as the main ones: Kr^T of their block during the
         // L / Mqk phase, then the Qd and Mqk record fragments of their token tile,
-        // built and stored during the inverse phase.
+        // built and stored during the inverse phase, then the Kr^T fragments of
+        // scan wavefront wave - 8 during the record phase.
         const int lane = tid0 & 63, l16 = lane & 15, lq = lane >> 4;
         for (int item = blockIdx.x; item < items; item += gridDim.x) {
             const int ci = chunk_of(item), h = item % H;
@@ -895,6 +884,14 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         rec + (size_t)(i < 4 ? i : tt) * Rec::WAVE + (i < 4 ? Rec::QD + tt * 1024 : Rec::MQ + (i - 4) * 1024)));
             }
             __syncthreads();                             // off-diagonal inverse
+            // the Kr^T fragments of scan wavefront wave - 8: (wave - 8, KR + (2 rt + ks) KB)
+            {
+                char *rec = p.rec + ((size_t)h * p.rec_stride + ci - p.cw0) * Rec::BYTES + lane * 16;
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    __builtin_nontemporal_store(kr_frag(wave & 3, f >> 1, f & 1, lane),
+                                                reinterpret_cast<f16x8 *>(rec + (size_t)(wave & 3) * Rec::WAVE + Rec::KR + f * 1024));
+            }
             __syncthreads();                             // record
         }
         return;
