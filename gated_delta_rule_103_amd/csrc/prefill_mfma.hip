@@ -455,8 +455,10 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = 16 * I + 4 * lq + i, sc = 16 * I + l16;
-                    // masked entries may hold inf / nan: select, do not scale
-                    if (sc < tr) sLI[tr * SL + sc] = sBeta[tr] * accL[i];
+                    // masked entries may hold inf / nan: select, do not scale; the
+                    // block's upper triangle and diagonal are stored as zeros (the
+                    // substitution below relies on them)
+                    sLI[tr * SL + sc] = sc < tr ? sBeta[tr] * accL[i] : 0.f;
                 }
             }
         } else {
@@ -556,28 +558,48 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                         }
                     }
                 for (int e = lane; e < 256; e += 64)
-                    if ((e & 15) >= (e >> 4)) sMqk[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<_Float16>(0.f);
+                    if ((e & 15) >= (e >> 4)) {
+                        sMqk[(16 * I + (e >> 4)) * SMQ + 16 * I + (e & 15)] = static_cast<_Float16>(0.f);
+                        sLI[(16 * I + (e >> 4)) * SL + 16 * I + (e & 15)] = 0.f;   // L_II's upper triangle and diagonal
+                    }
             }
         }
         // INV_II = (I + L_II)^{-1} of the diagonal blocks, as soon as L_II is final:
-        // wave = block, lane < 16 = column of INV_II, by column-oriented
-        // substitution: once x[sc] is final it is eliminated from every later row at
-        // once, so the updates of a step are independent and the L column reads
-        // (wave-uniform addresses, written by this wave) do not wait on the
-        // arithmetic. INV_II is stored transposed in the block's upper triangle;
-        // entries above the diagonal stay 0 (they only ever see x[sc] = 0).
-        if (wave < 4 && lane < 16) {
-            const int I = wave, col = lane;
-            float x[16];
+        // wave = block, by column-oriented substitution on all 64 lanes: lane
+        // 4 col + g holds rows g, g + 4, g + 8, g + 12 of column col of INV_II.
+        // Once x[sc] is final it is broadcast within the quad (DPP) and eliminated
+        // from the lane's four rows at once; L_II's zeros on and above the
+        // diagonal leave the rows at or above sc unchanged. The lane's four rows
+        // of L_II are read first (16-byte rows, written by this wave). INV_II is
+        // stored transposed in the block's upper triangle; entries above the
+        // diagonal stay 0 (they only ever see x[sc] = 0).
+        if (wave < 4) {
+            const int I = wave, col = lane >> 2, g = lane & 3;
+            const float *Lb = sLI + 16 * I * SL + 16 * I;    // L_II[tr][sc] = Lb[tr * SL + sc]
+            f32x4 Lr[4][4];
 #pragma unroll
-            for (int tr = 0; tr < 16; ++tr) x[tr] = (tr == col) ? 1.f : 0.f;
+            for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int sc = 0; sc < 15; ++sc)
+                for (int q = 0; q < 4; ++q) Lr[k][q] = *reinterpret_cast<const f32x4 *>(Lb + (g + 4 * k) * SL + 4 * q);
+            float x[4];
 #pragma unroll
-                for (int tr = sc + 1; tr < 16; ++tr) x[tr] -= sLI[(16 * I + tr) * SL + 16 * I + sc] * x[sc];
+            for (int k = 0; k < 4; ++k) x[k] = (g + 4 * k == col) ? 1.f : 0.f;
+            auto bcast = [&](auto Sc) {                      // x[sc] of this column, from lane 4 col + sc % 4
+                constexpr int sc = decltype(Sc)::value;
+                return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[sc >> 2]), 85 * (sc & 3), 0xf, 0xf, false));
+            };
+            auto eliminate = [&](auto Sc) {
+                constexpr int sc = decltype(Sc)::value;
+                const float xs = bcast(Sc);
 #pragma unroll
-            for (int tr = 0; tr < 16; ++tr)
-                if (tr >= col) sLI[(16 * I + col) * SL + 16 * I + tr] = x[tr];
+                for (int k = 0; k < 4; ++k) x[k] -= Lr[k][sc >> 2][sc & 3] * xs;
+            };
+            eliminate(IC<0>{}); eliminate(IC<1>{}); eliminate(IC<2>{}); eliminate(IC<3>{}); eliminate(IC<4>{});
+            eliminate(IC<5>{}); eliminate(IC<6>{}); eliminate(IC<7>{}); eliminate(IC<8>{}); eliminate(IC<9>{});
+            eliminate(IC<10>{}); eliminate(IC<11>{}); eliminate(IC<12>{}); eliminate(IC<13>{}); eliminate(IC<14>{});
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (g + 4 * k >= col) sLI[(16 * I + col) * SL + 16 * I + g + 4 * k] = x[k];
         }
         __syncthreads();
         fetch(next, 1);
