@@ -202,6 +202,7 @@ template <typename TB, bool VARLEN, bool GHEAD, bool NORM>
 __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
+    __shared__ int s_hand;               // item + 1 once INV_32^T is in the 1 / Gamma tile (inverse phase)
     static_assert(Lo::SIZE <= 163840, "LDS budget");
     __bf16 *sQs = reinterpret_cast<__bf16 *>(smem + Lo::QS);
     __bf16 *sKs = reinterpret_cast<__bf16 *>(smem + Lo::KS);
@@ -687,9 +688,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             };
             const int I = 2 + (wave >> 1), J = wave & 1;        // this wavefront's INV_IJ
             f32x4 inv10 = z4, inv32t = z4;
-            if (J == 0)                                         // INV_10 = -INV_11 (L_10 INV_00)
-                inv10 = -mm(z4, inv_rk(1), mm(z4, l_rk(1, 0), inv_kc(0)));
-            if (I == 3) {                                       // INV_32^T = -INV_22^T (L_32^T INV_33^T)
+            // INV_32^T = -INV_22^T (L_32^T INV_33^T), needed by wavefronts 2 and 3, is
+            // formed by wavefront 1, whose own block takes the fewest products, and
+            // handed over through LDS (the 1 / Gamma tile, dead in this phase) with
+            // the item's number as the flag; the readers wait for it only before
+            // their last product, and the writer reaches the flag with no barrier
+            // or wait on the way, so the bounded wait always ends.
+            if (wave == 1) {
                 f32x4 a, b;                                     // L_32^T[l16][k], INV_33^T[k][l16]
 #pragma unroll
                 for (int sl = 0; sl < 4; ++sl) {
@@ -697,8 +702,13 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     const float x = sLI[(48 + k0 + sl) * SL + 48 + l16];
                     b[sl] = k0 + sl > l16 ? 0.f : x;
                 }
-                inv32t = -mm(z4, inv_kc(2), mm(z4, a, b));
+                reinterpret_cast<f32x4 *>(sIGB)[lane] = -mm(z4, inv_kc(2), mm(z4, a, b));
+                asm volatile("" ::: "memory");                  // the tile's write stays before the flag's
+                if (lane == 0)                                  // (and LDS keeps a wavefront's order)
+                    __hip_atomic_store(&s_hand, item + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
+            if (J == 0)                                         // INV_10 = -INV_11 (L_10 INV_00)
+                inv10 = -mm(z4, inv_rk(1), mm(z4, l_rk(1, 0), inv_kc(0)));
             // P_XJ = L_XJ INV_JJ (+ L_X1 INV_10 when J == 0)
             const f32x4 bJ = inv_kc(J);
             auto p_of = [&](int X) {
@@ -708,7 +718,15 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             };
             const f32x4 p2 = p_of(2);
             f32x4 o = mm(z4, inv_rk(I), I == 2 ? p2 : p_of(3));
-            if (I == 3) o = mm(o, inv32t, p2);
+            if (I == 3) {
+                for (int it = 0; it < (1 << 22) &&
+                                 __hip_atomic_load(&s_hand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != item + 1;
+                     ++it)
+                    __builtin_amdgcn_s_sleep(1);
+                asm volatile("" ::: "memory");
+                inv32t = reinterpret_cast<const f32x4 *>(sIGB)[lane];
+                o = mm(o, inv32t, p2);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) sLI[(16 * J + l16) * SL + 16 * I + 4 * lq + i] = -o[i];
             // the blocks formed on the way that are stored once
@@ -795,6 +813,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         __syncthreads();      // LDS is restaged by the next item
     };
     if (tid0 < 4) sFlag[tid0] = 0;
+    if (tid0 == 0) s_hand = 0;
     __syncthreads();
     if (wave >= 8) {
         // Helper wavefronts 8-11 (block and token tile wave - 8), through the same
