@@ -202,7 +202,7 @@ template <typename TB, bool VARLEN, bool GHEAD, bool NORM>
 __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using Lo = PrepLds;
-    __shared__ int s_hand;               // item + 1 once INV_32^T is in the 1 / Gamma tile (inverse phase)
+    __shared__ int s_hand[2];            // item + 1 once INV_32^T / INV_10 are in the 1 / Gamma tile (inverse phase)
     static_assert(Lo::SIZE <= 163840, "LDS budget");
     __bf16 *sQs = reinterpret_cast<__bf16 *>(smem + Lo::QS);
     __bf16 *sKs = reinterpret_cast<__bf16 *>(smem + Lo::KS);
@@ -690,10 +690,25 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
             f32x4 inv10 = z4, inv32t = z4;
             // INV_32^T = -INV_22^T (L_32^T INV_33^T), needed by wavefronts 2 and 3, is
             // formed by wavefront 1, whose own block takes the fewest products, and
+            // INV_10, needed by wavefronts 0 and 2, by wavefront 0 first; both are
             // handed over through LDS (the 1 / Gamma tile, dead in this phase) with
-            // the item's number as the flag; the readers wait for it only before
-            // their last product, and the writer reaches the flag with no barrier
-            // or wait on the way, so the bounded wait always ends.
+            // the item's number as the flag. A reader waits only where it needs the
+            // block, and a writer reaches its flag with no barrier or wait on the
+            // way, so the bounded waits always end.
+            auto hand_over = [&](int slot, f32x4 v) {
+                reinterpret_cast<f32x4 *>(sIGB)[64 * slot + lane] = v;
+                asm volatile("" ::: "memory");                  // the tile's write stays before the flag's
+                if (lane == 0)                                  // (and LDS keeps a wavefront's order)
+                    __hip_atomic_store(&s_hand[slot], item + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            };
+            auto take_over = [&](int slot) {
+                for (int it = 0; it < (1 << 22) &&
+                                 __hip_atomic_load(&s_hand[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != item + 1;
+                     ++it)
+                    __builtin_amdgcn_s_sleep(1);
+                asm volatile("" ::: "memory");
+                return reinterpret_cast<const f32x4 *>(sIGB)[64 * slot + lane];
+            };
             if (wave == 1) {
                 f32x4 a, b;                                     // L_32^T[l16][k], INV_33^T[k][l16]
 #pragma unroll
@@ -702,29 +717,25 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
                     const float x = sLI[(48 + k0 + sl) * SL + 48 + l16];
                     b[sl] = k0 + sl > l16 ? 0.f : x;
                 }
-                reinterpret_cast<f32x4 *>(sIGB)[lane] = -mm(z4, inv_kc(2), mm(z4, a, b));
-                asm volatile("" ::: "memory");                  // the tile's write stays before the flag's
-                if (lane == 0)                                  // (and LDS keeps a wavefront's order)
-                    __hip_atomic_store(&s_hand, item + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                hand_over(0, -mm(z4, inv_kc(2), mm(z4, a, b)));
             }
-            if (J == 0)                                         // INV_10 = -INV_11 (L_10 INV_00)
+            if (wave == 0) {                                    // INV_10 = -INV_11 (L_10 INV_00)
                 inv10 = -mm(z4, inv_rk(1), mm(z4, l_rk(1, 0), inv_kc(0)));
+                hand_over(1, inv10);
+            }
             // P_XJ = L_XJ INV_JJ (+ L_X1 INV_10 when J == 0)
             const f32x4 bJ = inv_kc(J);
-            auto p_of = [&](int X) {
-                f32x4 acc = mm(z4, l_rk(X, J), bJ);
-                if (J == 0) acc = mm(acc, l_rk(X, 1), inv10);
-                return acc;
-            };
-            const f32x4 p2 = p_of(2);
-            f32x4 o = mm(z4, inv_rk(I), I == 2 ? p2 : p_of(3));
+            // the parts of P_2J and P_3J without INV_10 first
+            f32x4 p2 = mm(z4, l_rk(2, J), bJ), p3 = z4;
+            if (I == 3) p3 = mm(z4, l_rk(3, J), bJ);
+            if (J == 0) {
+                if (wave == 2) inv10 = take_over(1);
+                p2 = mm(p2, l_rk(2, 1), inv10);
+                if (I == 3) p3 = mm(p3, l_rk(3, 1), inv10);
+            }
+            f32x4 o = mm(z4, inv_rk(I), I == 2 ? p2 : p3);
             if (I == 3) {
-                for (int it = 0; it < (1 << 22) &&
-                                 __hip_atomic_load(&s_hand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != item + 1;
-                     ++it)
-                    __builtin_amdgcn_s_sleep(1);
-                asm volatile("" ::: "memory");
-                inv32t = reinterpret_cast<const f32x4 *>(sIGB)[lane];
+                inv32t = take_over(0);
                 o = mm(o, inv32t, p2);
             }
 #pragma unroll
@@ -813,7 +824,7 @@ __global__ __launch_bounds__(PTHR) void chunk_prep_kernel(PrepParams p) {
         __syncthreads();      // LDS is restaged by the next item
     };
     if (tid0 < 4) sFlag[tid0] = 0;
-    if (tid0 == 0) s_hand = 0;
+    if (tid0 < 2) s_hand[tid0] = 0;
     __syncthreads();
     if (wave >= 8) {
         // Helper wavefronts 8-11 (block and token tile wave - 8), through the same
