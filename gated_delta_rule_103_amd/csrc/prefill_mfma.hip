@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     constexpr int NT = TV / 16;
     constexpr int TEAM = D / TV;
     constexpr int VW = TV / 8;           // dwords of V per output thread and chunk (TV / 4 columns of one token)
-    static_assert(TV == 16 || TV == 32, "value columns per workgroup");
+    static_assert(TV == 16 || TV == 32 || TV == 64, "value columns per workgroup");
     _Float16 *sMh = reinterpret_cast<_Float16 *>(smem + Lo::M);
     _Float16 *sMl = sMh + TV * SMS;
     _Float16 *sUh = reinterpret_cast<_Float16 *>(smem + Lo::U);
@@ -1315,9 +1315,12 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
             const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0));
             f.vr[0] = x[0]; f.vr[1] = x[1];
         } else {
-            const u32x4 x = buf_ld16<u32x4>(rv, v_off, 0);
 #pragma unroll
-            for (int i = 0; i < VW; ++i) f.vr[i] = x[i];
+            for (int q = 0; q < VW / 4; ++q) {
+                const u32x4 x = buf_ld16<u32x4>(rv, v_off + 16 * q, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f.vr[4 * q + i] = x[i];
+            }
         }
         __builtin_amdgcn_sched_barrier(0x048F);
     };
@@ -1524,16 +1527,18 @@ hipError_t run(const PrefillArgs &a) {
         {{chunk_prep_kernel<TB, true, false, false>, chunk_prep_kernel<TB, true, false, true>},
          {chunk_prep_kernel<TB, true, true, false>, chunk_prep_kernel<TB, true, true, true>}}};
     const PrepKern prep_kern = kerns[varlen][a.g_head][a.qk_norm];
-    // 16 value columns per scan workgroup, or 32 when the 16-column workgroups
-    // would fill the CUs four times over or more (many chains, e.g. packed
-    // batches): a CU then reads each record once per 32 columns instead of per 16
+    // 16 value columns per scan workgroup, 32 when the 16-column workgroups
+    // would fill the CUs four times over or more, 64 when sixteen times (many
+    // chains, e.g. packed batches): the scan is then bound by the CUs' total
+    // work rather than by its chains' length, and a CU reads each record once
+    // per 32 or 64 columns instead of per 16
     const int chains = a.N * a.H;
-    const bool wide = (long long)chains * (D / 16) >= 4LL * cus;
-    const int team = wide ? D / 32 : D / 16;
+    const int tv = (long long)chains * (D / 16) >= 16LL * cus ? 64 : (long long)chains * (D / 16) >= 4LL * cus ? 32 : 16;
+    const int team = D / tv;
     const unsigned scan_blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
     using ScanKern = void (*)(ScanParams);
-    const ScanKern scan_kern = wide ? chunk_scan_kernel<32, TO> : chunk_scan_kernel<16, TO>;
-    const int scan_lds = wide ? ScanLds<32>::SIZE : ScanLds<16>::SIZE;
+    const ScanKern scan_kern = tv == 64 ? chunk_scan_kernel<64, TO> : tv == 32 ? chunk_scan_kernel<32, TO> : chunk_scan_kernel<16, TO>;
+    const int scan_lds = tv == 64 ? ScanLds<64>::SIZE : tv == 32 ? ScanLds<32>::SIZE : ScanLds<16>::SIZE;
     // set on every call (idempotent; no process-wide "already set" flag to race on)
     if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prep_kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
