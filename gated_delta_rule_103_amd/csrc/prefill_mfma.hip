@@ -194,6 +194,28 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(SeqView sv, int2 *meta,
     meta[ci] = int2{tok0, min(C, sv.seq_end(n) - tok0)};
 }
 
+// Packed sequences (N <= ORDER_MAX): order[rank] = n, ranked by decreasing chunk
+// count, ties by index (a strict total order, so order is a permutation). The
+// scan maps its chains through it: its workgroups are dispatched in block order,
+// so the longest chains start first and the short ones fill in behind them
+// (longest-processing-time-first list scheduling) instead of the last long
+// sequences starting when the CUs are nearly drained.
+constexpr int ORDER_MAX = 1024;
+__global__ __launch_bounds__(ORDER_MAX) void chain_order_kernel(SeqView sv, int32_t *order) {
+    __shared__ int s_nc[ORDER_MAX];
+    const int N = sv.N, n = threadIdx.x;
+    if (n < N) s_nc[n] = sv.first_chunk(n + 1) - sv.first_chunk(n);
+    __syncthreads();
+    if (n >= N) return;
+    const int c = s_nc[n];
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+        const int d = s_nc[m];
+        rank += (d > c) || (d == c && m < n);
+    }
+    order[rank] = n;
+}
+
 // GHEAD: one log-decay per (token, head), g [T][H] or none (nullptr), instead
 // of one per key channel. NORM: q and k are L2-normalised over the channels on
 // the fly: 1/||q_t||, 1/||k_t|| (fp32, from the staged bf16 rows) scale the
@@ -1015,6 +1037,10 @@ struct ScanParams {
     // one whose chunks began before it takes its state from there.
     float *S_run;
     int cw0, cwn;
+    // packed sequences: order[i] = the sequence with the i-th most chunks (ties
+    // by index), so that the workgroups of the longest chains are dispatched
+    // first; nullptr: sequence order
+    const int32_t *order;
 };
 
 // exponent e with R 2^e in [64, 128) (R > 0), clamped; 7 for R == 0
@@ -1065,7 +1091,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     const int member = r % TEAM, grp = r / TEAM;
     const int chain = grp * 8 + xcd;
     if (chain >= p.chains) return;
-    const int H = p.H, n = chain / H, h = chain % H;
+    const int H = p.H, n = p.order ? p.order[chain / H] : chain / H, h = chain % H;
     const int col0 = member * TV;
     const int start = p.sv.seq_start(n), end = p.sv.seq_end(n);
     const int nch = (end - start + C - 1) / C, c0 = p.sv.first_chunk(n);
@@ -1460,8 +1486,9 @@ hipError_t device_cus(int *cus) {
     return e;
 }
 
-// workspace: chunk offsets (N + 1 int32), the chunk table (maxc int2), records
-size_t ws_offs(int N) { return ((sizeof(int32_t) * (size_t)(N + 1) + 255) / 256) * 256; }
+// workspace: chunk offsets (N + 1 int32) and the chains' order (N int32), the
+// chunk table (maxc int2), records
+size_t ws_offs(int N) { return ((sizeof(int32_t) * (size_t)(2 * N + 1) + 255) / 256) * 256; }
 size_t ws_meta(long long maxc) { return ((sizeof(int2) * (size_t)maxc + 255) / 256) * 256; }
 
 // One long sequence runs as a pipeline over windows of WIN chunks: the prep of
@@ -1518,6 +1545,11 @@ hipError_t run(const PrefillArgs &a) {
                            sv, meta, (int)maxc);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.N > 1 && a.N <= ORDER_MAX) {
+            hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(ORDER_MAX), 0, a.stream, sv, chunk_off + a.N + 1);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     // kernel variant [varlen][per-head gate][L2-normalised q, k]
     using PrepKern = void (*)(PrepParams);
@@ -1560,7 +1592,8 @@ hipError_t run(const PrefillArgs &a) {
     };
     auto scan = [&](long long cw0, long long cwn, const char *slot, hipStream_t st) {
         ScanParams sp{static_cast<const bf16_t *>(a.v), a.S0, a.out, a.S_out, sv, a.H, chains, slot, cwn,
-                      SnapView{a.snaps, a.snap_every, a.max_snaps}, S_run, (int)cw0, (int)cwn};
+                      SnapView{a.snaps, a.snap_every, a.max_snaps}, S_run, (int)cw0, (int)cwn,
+                      varlen && a.N > 1 && a.N <= ORDER_MAX ? chunk_off + a.N + 1 : nullptr};
         hipLaunchKernelGGL(scan_kern, dim3(scan_blocks), dim3(SCAN_THR), scan_lds, st, sp);
         return hipGetLastError();
     };

@@ -177,6 +177,18 @@ def test_prefill_most_chains_64_column_scan_tiles(slow):
     run_and_check(p, TOL_BF16, label=f"{16 * len(lengths)} chains, 64-column scan tiles{' (slow decay)' if slow else ''}")
 
 
+def test_prefill_more_sequences_than_the_chain_order_table():
+    """Packed batches of up to 1,024 sequences have their chains scanned longest
+    first (through a device-side order table); more sequences than that keep
+    sequence order. 1,100 ragged sequences (empty ones among them) x 2 heads, nonzero
+    S0: every token, head and final state against the oracle."""
+    rng = np.random.default_rng(47)
+    lengths = [int(x) for x in rng.integers(0, 150, size=1100)]
+    lengths[5] = lengths[700] = 0
+    p = inputs.prefill(2, 128, lengths=lengths, C=64, io="bf16", s0_std=0.3, seed=47)
+    run_and_check(p, TOL_BF16, label="1,100 sequences (sequence order)")
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_prefill_varlen_edges(io):
     """Packed sequences with zero- and one-token members and a nonzero initial state."""
