@@ -1390,14 +1390,19 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
     // 128-byte line of its share of the record, so that the records' lines are
     // in L2 when the operand loads arrive. The touched values are folded into a
     // register one step later (that load is then long complete) and kept alive
-    // to the end by an empty asm that takes them as input.
+    // to the end by an empty asm that takes them as input. Not with 64-column
+    // workgroups: they run where the chains fill the CUs many times over, 16
+    // chains per XCD, and three chunks of their records in flight would nearly
+    // fill the XCD's 4 MB L2, so that lines were evicted before the team's
+    // second workgroup read them.
     constexpr int LPW = Rec::DG / 128 / (4 * TEAM);                 // lines per wavefront
     const int touch_off = ((member * 4 + w4) * LPW + lane % LPW) * 128;  // < Rec::DG
     uint32_t touch_acc = 0, touch_prev = 0;
     auto ostep = [&](OFrags &f, int j, OFrags &nf, int nj) {
         const int bsel = j & 1;
         touch_acc ^= touch_prev;
-        touch_prev = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(j + 3, last)), touch_off, 0, 0);
+        if constexpr (TV < 64)
+            touch_prev = __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(j + 3, last)), touch_off, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         vissue(min(j + 3, last), f);     // this buffer's chunk after next: j + 3
         // o^T (part) = M^T Qd^T from the state at the chunk start (in LDS since
