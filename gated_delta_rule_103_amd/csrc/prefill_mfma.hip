@@ -1564,13 +1564,22 @@ hipError_t run(const PrefillArgs &a) {
         {{chunk_prep_kernel<TB, true, false, false>, chunk_prep_kernel<TB, true, false, true>},
          {chunk_prep_kernel<TB, true, true, false>, chunk_prep_kernel<TB, true, true, true>}}};
     const PrepKern prep_kern = kerns[varlen][a.g_head][a.qk_norm];
-    // 16 value columns per scan workgroup, 32 when the 16-column workgroups
-    // would fill the CUs four times over or more, 64 when sixteen times (many
-    // chains, e.g. packed batches): the scan is then bound by the CUs' total
-    // work rather than by its chains' length, and a CU reads each record once
-    // per 32 or 64 columns instead of per 16
+    // Value columns per scan workgroup: one workgroup fits on a CU, so the
+    // scan takes about (rounds of workgroups over the CUs) x (steps of the
+    // longest chain) x (time of a step). A step of a 16-, 32- or 64-column
+    // workgroup takes about 1.3, 1.8 and 2.9 us on MI355X: wider tiles read each
+    // record once for more columns, narrower ones put more CUs on a chain. The
+    // width with the fewest rounds x step time is taken (the narrower on a tie).
     const int chains = a.N * a.H;
-    const int tv = (long long)chains * (D / 16) >= 16LL * cus ? 64 : (long long)chains * (D / 16) >= 4LL * cus ? 32 : 16;
+    int tv = 16;
+    {
+        long long best = -1;
+        for (const int w : {16, 32, 64}) {
+            const long long rounds = ((long long)chains * (D / w) + cus - 1) / cus;
+            const long long cost = rounds * (w == 16 ? 13 : w == 32 ? 18 : 29);
+            if (best < 0 || cost < best) { best = cost; tv = w; }
+        }
+    }
     const int team = D / tv;
     const unsigned scan_blocks = (unsigned)((chains + 7) / 8) * 8u * (unsigned)team;
     using ScanKern = void (*)(ScanParams);

@@ -151,10 +151,11 @@ def test_prefill_ragged_lengths(D, C, io):
 
 @pytest.mark.parametrize("slow", [False, True])
 def test_prefill_many_chains_wide_scan_tiles(slow):
-    """Packed batches with many (sequence, head) chains take the scan's 32-column
-    workgroups (4 x CUs <= chains x 8 < 16 x CUs): 12 ragged sequences x 16 heads
-    = 192 chains, nonzero S0, a zero-length and a one-token sequence among them,
-    and a slow-decay variant where the state carries across chunks."""
+    """Packed batches with many (sequence, head) chains: 12 ragged sequences x 16
+    heads = 192 chains take the scan's 32-column workgroups on 256 CUs (three
+    rounds of 32-column workgroups cost less than two of 64-column ones), nonzero
+    S0, a zero-length and a one-token sequence among them, and a slow-decay
+    variant where the state carries across chunks."""
     lengths = [130, 0, 64, 1, 257, 191, 65, 128, 320, 63, 200, 96]
     p = inputs.prefill(16, 128, lengths=lengths, C=64, io="bf16", s0_std=0.3, seed=41,
                        shift=-4.0 if slow else 2.0)
@@ -163,10 +164,11 @@ def test_prefill_many_chains_wide_scan_tiles(slow):
 
 @pytest.mark.parametrize("slow", [False, True])
 def test_prefill_most_chains_64_column_scan_tiles(slow):
-    """Packed batches with at least twice as many chains as CUs take the scan's
-    64-column workgroups (chains x 8 >= 16 x CUs): the ragged lengths above
-    repeated until 16 heads give that many chains (zero-length and one-token
-    sequences among them), nonzero S0, and slow decay; fp32 and bf16 outputs."""
+    """Packed batches with twice as many chains as CUs take the scan's 64-column
+    workgroups (one round of them against two of 32-column ones): the ragged
+    lengths above repeated until 16 heads give that many chains (zero-length and
+    one-token sequences among them), nonzero S0, and slow decay; fp32 and bf16
+    outputs."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     base = [130, 0, 64, 1, 257, 191, 65, 128, 320, 63, 200, 96]
     n = -(-2 * cus // 16)                     # sequences for 16 heads x n >= 2 x CUs
