@@ -85,6 +85,17 @@ def test_snapshots_many_chains_wide_scan_tiles():
     _check(p, 64, 4, TOL_BF16, "many chains, wide scan tiles")
 
 
+def test_snapshots_most_chains_64_column_scan_tiles():
+    """Twice as many chains as CUs (the ragged lengths above repeated, 16 heads) take
+    the scan's 64-column workgroups, dispatched longest sequence first."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    base = [130, 0, 64, 1, 257, 191, 65, 128, 320, 63, 200, 96]
+    n = -(-2 * cus // 16)
+    lengths = [base[i % len(base)] for i in range(n)]
+    p = inputs.prefill(16, 128, lengths=lengths, C=64, io="bf16", s0_std=0.02, gate="slow", seed=76)
+    _check(p, 64, 4, TOL_BF16, f"{16 * n} chains, 64-column scan tiles")
+
+
 def test_snapshots_f32_path():
     p = inputs.prefill(2, 64, B=1, T=150, C=16, io="f32", seed=73)
     _check(p, 32, 6, TOL_F32, "fp32 path, D=64, C=16")
