@@ -1010,7 +1010,11 @@ constexpr int SCAN_THR = 2 * NREC;       // ... and as many output wavefronts
 // a plain padded row stride costs one extra cycle per 16 lanes on these reads.
 constexpr int SMS = D;                   // fp16 row of the state   [col][128], blocks ^ (col & 15)
 constexpr int SUS = C;                   // fp16 row of U           [col][64],  blocks ^ (col & 7)
-constexpr int SVT = C;                   // bf16 row of the V tile  [col][64],  blocks ^ (col & 7)
+constexpr int SVT = C;                   // bf16 row of the V tile  [col][64],  blocks ^ vsw(col)
+// the V tile's block swizzle: the column's low three bits XOR-ed with the next
+// three, so that the four lanes staging one token (columns TV / 4 apart) write
+// to four distinct blocks at every tile width
+__device__ __forceinline__ int vsw(int col) { return (col ^ (col >> 3)) & 7; }
 
 template <int TV>
 struct ScanLds {
@@ -1193,7 +1197,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8 vv = lds8(reinterpret_cast<const __bf16 *>(sV) + bsel * TV * SVT + (16 * nt + l16) * SVT +
-                                           8 * ((4 * ks + lq) ^ (l16 & 7)));
+                                           8 * ((4 * ks + lq) ^ vsw(16 * nt + l16)));
                     f16x8 vb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) vb[e] = static_cast<_Float16>(bf2f(vv[e]) * sc);
@@ -1375,7 +1379,7 @@ __global__ __launch_bounds__(SCAN_THR) void chunk_scan_kernel(ScanParams p) {
             const uint32_t wv = f.vr[e >> 1];
             const bf16_t x = static_cast<bf16_t>(e & 1 ? wv >> 16 : wv & 0xffffu);
             const int c = c0 + e;
-            dst[c * SVT + 8 * ((t >> 3) ^ (c & 7))] = x;
+            dst[c * SVT + 8 * ((t >> 3) ^ vsw(c))] = x;
             vm = fmaxf(vm, fabsf(bf16_to_f32(x)));
         }
         vm = wave_max(vm);
